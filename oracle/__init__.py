@@ -1,0 +1,225 @@
+"""CPU oracle for the row-parallel matmul + reduce hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product path
+(``row_matmul_reduce_amd``) never imports, loads or calls it, and the two share
+no code: the oracle is plain C (``rpl_oracle.c``), built with gcc, wrapped here
+with ctypes and numpy.
+
+Every function computes the unfused definition in fp64 (see the header of
+``rpl_oracle.c`` for the passages followed and the readings taken).  Inputs are
+numpy arrays: bfloat16 tensors are carried as ``uint16`` bit patterns.
+
+Parity status of each function (what pins it lives in tests/test_oracle_pins.py):
+  partial_rows           pinned: exact rational brute force, numpy fp64 GEMM,
+                         one-hot / small-integer closed forms, hand-worked golden
+  reduce_chunk_rmsnorm   pinned: 60-digit decimal brute force, RMS invariant,
+                         scale invariance, zero row, hand-worked golden
+  w8a8_rows              pinned: numpy int64 GEMM, sign symmetry, numpy float32
+                         dequant in the same operation order
+  f64_to_bf16            pinned: exact rational nearest-even search
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rpl_oracle.c")
+_LIB = os.path.join(_HERE, "librpl_oracle.so")
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+             "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc a C oracle source into a shared object (no fast-math, no FMA contraction)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle next to its source."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def load(path: str):
+    """Load an oracle shared object and declare its C signatures."""
+    L = ctypes.CDLL(path)
+    L.orc_bf16_to_f64.restype = ctypes.c_double
+    L.orc_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    L.orc_f64_to_bf16.restype = ctypes.c_uint16
+    L.orc_f64_to_bf16.argtypes = [ctypes.c_double]
+    L.orc_f32_to_bf16.restype = ctypes.c_uint16
+    L.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.orc_partial_rows.restype = ctypes.c_int
+    L.orc_partial_rows.argtypes = [_p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _p]
+    L.orc_reduce_chunk_rmsnorm.restype = ctypes.c_int
+    L.orc_reduce_chunk_rmsnorm.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p,
+                                           ctypes.c_float, _p, _p, _p, _p]
+    L.orc_w8a8_rows.restype = ctypes.c_int
+    L.orc_w8a8_rows.argtypes = [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+    L.orc_num_threads.restype = ctypes.c_int
+    L.orc_set_num_threads.argtypes = [ctypes.c_int]
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = load(_LIB)
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check2d(a: np.ndarray, dtype, name: str):
+    if a.dtype != dtype or a.ndim != 2:
+        raise TypeError(f"{name}: expected 2-D {np.dtype(dtype)}, got {a.dtype} {a.shape}")
+    if a.strides[1] != a.itemsize:
+        raise ValueError(f"{name}: rows must be contiguous")
+    return a.strides[0] // a.itemsize
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def set_num_threads(t: int) -> None:
+    lib().orc_set_num_threads(int(t))
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(lib().orc_f64_to_bf16(float(v)))
+
+
+def bf16_to_f64(b: int) -> float:
+    return float(lib().orc_bf16_to_f64(int(b)))
+
+
+def f64_to_bf16_array(a: np.ndarray) -> np.ndarray:
+    f = lib().orc_f64_to_bf16
+    flat = np.asarray(a, dtype=np.float64).ravel()
+    return np.array([f(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(a))
+
+
+def bf16_to_f64_array(b: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (a float32 with zero low half)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def partial_rows(x: np.ndarray, w: np.ndarray, m: int, rows=None, tp: int = 1,
+                 want_f64: bool = False):
+    """Rank partial rows: bf16(x[r] . w[j]) for r < m, zero for pad rows.
+
+    x: [>=m, k] uint16 (bf16 bits) -- only rows < m are read;  w: [n, k] uint16.
+    rows: output row indices into the padded [M_pad, n] output (default: all
+    M_pad = ceil(m/tp)*tp rows).  Returns uint16 [len(rows), n] (and the fp64
+    values when want_f64).
+    """
+    ldx = _check2d(x, np.uint16, "x")
+    ldw = _check2d(w, np.uint16, "w")
+    k = x.shape[1]
+    if w.shape[1] != k:
+        raise ValueError("x and w disagree on k")
+    n = w.shape[0]
+    m_pad = -(-m // tp) * tp
+    if rows is None:
+        rows = np.arange(m_pad, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= m_pad):
+        raise ValueError("row index outside the padded output")
+    live = rows[rows < m]
+    if live.size and int(live.max()) >= x.shape[0]:
+        raise ValueError("x has fewer rows than the requested output rows need")
+    out = np.empty((rows.size, n), dtype=np.uint16)
+    f64 = np.empty((rows.size, n), dtype=np.float64) if want_f64 else None
+    rc = lib().orc_partial_rows(_ptr(x), ldx, _ptr(w), ldw, m, n, k, _ptr(rows), rows.size,
+                                _ptr(out), _ptr(f64))
+    if rc != 0:
+        raise RuntimeError(f"orc_partial_rows failed: {rc}")
+    return (out, f64) if want_f64 else out
+
+
+def reduce_chunk_rmsnorm(partials, residual: np.ndarray, gamma: np.ndarray, eps: float,
+                         want_f64: bool = False):
+    """Sum of TP bf16 partial chunks + residual, then RMSNorm.
+
+    partials: list of [m_chunk, n] uint16 arrays (same row stride);
+    residual: [m_chunk, n] uint16; gamma: [n] uint16.
+    Returns (y, residual_out) as uint16, plus (h_f64, y_f64) when want_f64.
+    """
+    tp = len(partials)
+    if tp < 1:
+        raise ValueError("need at least one partial")
+    ldp = _check2d(partials[0], np.uint16, "partials[0]")
+    m_chunk, n = partials[0].shape
+    for i, p in enumerate(partials):
+        if _check2d(p, np.uint16, f"partials[{i}]") != ldp or p.shape != (m_chunk, n):
+            raise ValueError("partials must share shape and row stride")
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    if residual.shape != (m_chunk, n) or gamma.shape != (n,):
+        raise ValueError("residual/gamma shape mismatch")
+    ptrs = (ctypes.c_void_p * tp)(*[p.ctypes.data for p in partials])
+    y = np.empty((m_chunk, n), dtype=np.uint16)
+    ro = np.empty((m_chunk, n), dtype=np.uint16)
+    hf = np.empty((m_chunk, n), dtype=np.float64) if want_f64 else None
+    yf = np.empty((m_chunk, n), dtype=np.float64) if want_f64 else None
+    rc = lib().orc_reduce_chunk_rmsnorm(ctypes.cast(ptrs, ctypes.c_void_p), tp, ldp, m_chunk, n,
+                                        _ptr(residual), _ptr(gamma), float(eps),
+                                        _ptr(y), _ptr(ro), _ptr(hf), _ptr(yf))
+    if rc != 0:
+        raise RuntimeError(f"orc_reduce_chunk_rmsnorm failed: {rc}")
+    return (y, ro, hf, yf) if want_f64 else (y, ro)
+
+
+def w8a8_rows(xq: np.ndarray, sx: np.ndarray, wq: np.ndarray, sw: np.ndarray, m: int,
+              rows=None, tp: int = 1):
+    """int8 x int8 -> exact int32 accumulators and the bf16 dequantised output.
+
+    Returns (out uint16 [len(rows), n], acc int32 [len(rows), n]).
+    """
+    ldx = _check2d(xq, np.int8, "xq")
+    ldw = _check2d(wq, np.int8, "wq")
+    k = xq.shape[1]
+    if wq.shape[1] != k:
+        raise ValueError("xq and wq disagree on k")
+    n = wq.shape[0]
+    sx = np.ascontiguousarray(sx, dtype=np.float32)
+    sw = np.ascontiguousarray(sw, dtype=np.float32)
+    if sw.shape != (n,) or sx.shape[0] < min(m, xq.shape[0]):
+        raise ValueError("scale shape mismatch")
+    m_pad = -(-m // tp) * tp
+    if rows is None:
+        rows = np.arange(m_pad, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= m_pad):
+        raise ValueError("row index outside the padded output")
+    out = np.empty((rows.size, n), dtype=np.uint16)
+    acc = np.empty((rows.size, n), dtype=np.int32)
+    rc = lib().orc_w8a8_rows(_ptr(xq), ldx, _ptr(sx), _ptr(wq), ldw, _ptr(sw), m, n, k,
+                             _ptr(rows), rows.size, _ptr(out), _ptr(acc))
+    if rc == 2:
+        raise OverflowError("int32 accumulator overflow")
+    if rc != 0:
+        raise RuntimeError(f"orc_w8a8_rows failed: {rc}")
+    return out, acc

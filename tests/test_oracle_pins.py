@@ -1,0 +1,86 @@
+"""CPU-only: pin the oracle to facts outside itself, and show the pins bite.
+
+The second half plants plausible mistakes in copies of the oracle's C source
+(a dropped term, a wrong sign, a transposed operand, a wrong mean, eps outside
+the root, ties rounded away from zero, a missing subnormal clamp, a dropped
+residual, a reordered dequantisation), compiles each copy with gcc and checks
+that at least one pin fails for every one of them.
+"""
+import os
+import shutil
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_checks as oc
+
+pytestmark = []
+
+
+@pytest.mark.parametrize("check", oc.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(orc, check):
+    check(orc)
+
+
+def check_w8a8_dequant_many(orc):
+    """Many outputs so that an fp32 operation-order slip shows in the bf16 result."""
+    import torch
+    rng = np.random.default_rng(81)
+    m, k, n = 512, 32, 1024
+    xq = rng.integers(-127, 128, (m, k), dtype=np.int8)
+    wq = rng.integers(-127, 128, (n, k), dtype=np.int8)
+    sx = rng.uniform(1e-3, 2e-2, m).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, n).astype(np.float32)
+    out, acc = orc.w8a8_rows(xq, sx, wq, sw, m)
+    deq = (acc.astype(np.float32) * sx[:, None]) * sw[None, :]
+    ref = torch.from_numpy(deq).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out, ref)
+
+
+def test_w8a8_dequant_many(orc):
+    check_w8a8_dequant_many(orc)
+
+
+MUTANTS = [
+    ("dropped_last_k_term",
+     "for (int64_t kk = 0; kk < k; ++kk)\n                    s += orc_bf16",
+     "for (int64_t kk = 0; kk < k - 1; ++kk)\n                    s += orc_bf16"),
+    ("partial_sum_sign",
+     "acc += orc_bf16_to_f64(partials[s][i * ldp + j]);",
+     "acc += (s == 1 ? -1.0 : 1.0) * orc_bf16_to_f64(partials[s][i * ldp + j]);"),
+    ("transposed_weight",
+     "s += orc_bf16_to_f64(xr[kk]) * orc_bf16_to_f64(wr[kk]);",
+     "s += orc_bf16_to_f64(xr[kk]) * orc_bf16_to_f64(w[(kk * n + j) % (n * k)]);"),
+    ("mean_over_n_minus_1", "double ms = sumsq / (double)n;", "double ms = sumsq / (double)(n > 1 ? n - 1 : 1);"),
+    ("eps_outside_sqrt", "double denom = sqrt(ms + deps);", "double denom = sqrt(ms) + deps;"),
+    ("ties_away_from_zero", "double r = nearbyint(q);", "double r = floor(q + 0.5);"),
+    ("no_subnormal_clamp", "if (binade < -126) binade = -126;", ""),
+    ("residual_dropped_from_new_residual",
+     "if (residual_out) residual_out[i * n + j] = orc_f64_to_bf16(h);",
+     "if (residual_out) residual_out[i * n + j] = orc_f64_to_bf16(acc);"),
+    ("dequant_scales_multiplied_first",
+     "volatile float v = u * sw[j];",
+     "volatile float v = t * (((r < m) ? sx[r] : 0.0f) * sw[j]);"),
+    ("w8a8_sign_of_weight",
+     "s += (int64_t)xr[kk] * (int64_t)wr[kk];",
+     "s += (int64_t)xr[kk] * (int64_t)(kk == 0 ? -wr[kk] : wr[kk]);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, monkeypatch, name, old, new):
+    src = open(oracle._SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(mutated)
+    so = oracle.compile_source(str(path), str(tmp_path / f"mut_{name}.so"))
+    monkeypatch.setattr(oracle, "_lib", oracle.load(so))
+    failed = []
+    for check in oc.ALL_CHECKS + [check_w8a8_dequant_many]:
+        try:
+            check(oracle)
+        except (AssertionError, OverflowError, RuntimeError, ValueError):
+            failed.append(check.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
