@@ -1,0 +1,196 @@
+/*
+ * rpl.h -- C ABI of the row-parallel matmul + reduce library (librpl.so),
+ * native to AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, on one GPU, one tensor-parallel rank's share of the
+ * RowParallelLinear layer and the epilogue that the rank runs on the token
+ * chunk it receives:
+ *
+ *   rpl_partial               bf16 partial product of the rank's K-shard, laid
+ *                             out as reduce-scatter token chunks;
+ *   rpl_reduce_chunk_rmsnorm  sum of all ranks' partials for one token chunk
+ *                             (what a reduce-scatter delivers), residual add,
+ *                             RMSNorm;
+ *   rpl_w8a8_partial          the int8 x int8 (w8a8 dynamic-quant) variant of
+ *                             the partial, dequantised to bf16.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [FC1]  xLLM pull request #1890, "feat: add FlashComm1 and MMRS fusion support
+ *          for Qwen3.5 NPU": Summary; "MMRS Integration"; review thread diff
+ *          excerpts of RowParallelLinear and of the sequence pad/shard helpers.
+ *   [MMAR] vllm-ascend pull request #1926, "[Feature]: implement the fusion of
+ *          allreduce and matmul in prefill phase when tp is enabled": PR
+ *          description.
+ *   [910C] Dewu tech blog, "国产算力·昇腾 910C 大模型推理优化（下）：源码修改与算子优化",
+ *          communication-fusion section (the 910C fused o_proj matmul +
+ *          AllReduce + residual add + RMSNorm operator and its two-level
+ *          fallback) and the "small ops" section (RMSNorm weight 1+w).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor pointers are DEVICE pointers, owned by the caller (for instance
+ *    allocated by PyTorch).  The library allocates nothing, keeps no state
+ *    between calls, never synchronises and never aborts.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  Calls on different streams are independent; calls whose
+ *    buffers overlap must be ordered by the caller.
+ *  - bfloat16 values travel as their 16-bit patterns (rpl_bf16).  Matrices are
+ *    row-major; "ld" is a row stride in ELEMENTS.
+ *  - Tensor-parallel padding follows [FC1] (review thread, pad/shard helpers):
+ *    M tokens are padded to M_pad = ceil(M / tp) * tp rows and chunk c
+ *    (the rows rank c receives) is rows [c * M_pad/tp, (c + 1) * M_pad/tp).
+ *  - m == 0 (an empty batch) is valid: RPL_OK, nothing is enqueued, and the
+ *    row-indexed pointers (activations, their scales, outputs, partials,
+ *    residuals) may then be NULL; the layer's parameters (weights, weight
+ *    scales, gamma) are always required.
+ *  - Arguments are checked on the host, in the order of the status codes
+ *    below, before any HIP call.  On any status other than RPL_OK the outputs
+ *    are untouched (the fallback convention of [FC1] "MMRS Integration" and of
+ *    the [910C] operator's guard: an unsupported call leaves the caller free to
+ *    run the unfused composition instead).  Faults of an enqueued kernel, if
+ *    any, surface at the caller's next synchronisation of the stream.
+ */
+#ifndef RPL_H
+#define RPL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t rpl_bf16; /* bfloat16 bit pattern */
+
+typedef enum {
+    RPL_OK = 0,
+    RPL_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    RPL_ERR_INVALID = 2,     /* bad size / stride / eps, or overlapping outputs     */
+    RPL_ERR_UNSUPPORTED = 3, /* valid but outside what the kernels handle: see each */
+    RPL_ERR_LAUNCH = 4       /* the HIP launch itself reported an error             */
+} rpl_status;
+
+/* Largest tensor-parallel degree accepted by every call. */
+#define RPL_MAX_TP 16
+
+/*
+ * rpl_partial -- one rank's bf16 partial product over its K-shard.
+ *
+ * [FC1] review thread (RowParallelLinear MMRS path): the rank's input is
+ * [tokens, K_shard], its weight is stored [N, K_shard] and the output has
+ * N = weight.size(0) columns; [MMAR] PR description: the partials of all ranks
+ * are summed (all-reduce) -- see rpl_reduce_chunk_rmsnorm.
+ *
+ *   out[r, j] = bf16_rne( sum_{k < K} x[r, k] * w[j, k] )   for r < m
+ *   out[r, j] = 0                                           for m <= r < M_pad
+ * accumulated in fp32 (any summation order), rounded once to bf16, nearest-even.
+ *
+ * x    [m, k] bf16, row stride ldx >= k     (the rank's activation shard)
+ * w    [n, k] bf16, row stride ldw >= k     (nn.Linear weight shard, K-contiguous)
+ * out  [M_pad, n] bf16, contiguous (row stride n) = [tp][M_pad/tp][n] chunks;
+ *      must not overlap x or w
+ * m >= 0 tokens; n >= 1; k >= 1; 1 <= tp <= RPL_MAX_TP.
+ *
+ * RPL_ERR_NULL        w is NULL, or m > 0 and x or out is NULL
+ * RPL_ERR_INVALID     m < 0, n < 1, k < 1, tp < 1, ldx < k, ldw < k, out overlaps x/w
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; k, n, ldx or ldw not a multiple of 8;
+ *                     any pointer not 16-byte aligned; m, n or k >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed (e.g. no gfx950 device)
+ */
+rpl_status rpl_partial(const rpl_bf16 *x, int64_t ldx,
+                       const rpl_bf16 *w, int64_t ldw,
+                       rpl_bf16 *out,
+                       int64_t m, int64_t n, int64_t k, int32_t tp,
+                       void *stream);
+
+/*
+ * rpl_reduce_chunk_rmsnorm -- what rank c does with the token chunk it
+ * receives: the sum of every rank's partial for that chunk, residual add,
+ * RMSNorm.
+ *
+ * [FC1] Summary and review thread: with sequence parallelism the row-parallel
+ * reduction is a reduce-scatter along tokens, the residual is sharded the same
+ * way, and add + RMSNorm run on the local token chunk only.  [910C]
+ * communication-fusion section: after the cross-rank sum, the residual is
+ * added, the sum becomes the next residual, and RMSNorm takes the row's sum of
+ * squares, its reciprocal root, and scales by the weight.  For the Gemma form
+ * whose weight is 1+w ([910C] "small ops"), pass gamma = 1+w.
+ *
+ *   h[i, j]            = sum_{s < tp} partials[s][i, j] + residual[i, j]   (fp32)
+ *   residual_out[i, j] = bf16_rne(h[i, j])
+ *   y[i, j]            = bf16_rne( gamma[j] * h[i, j] / sqrt(mean_j(h[i, :]^2) + eps) )
+ * h is not rounded before the norm.  With m_chunk = M_pad (tp partials of all
+ * rows) this is the all-reduce form of [MMAR].
+ *
+ * partials      HOST array of tp DEVICE pointers, each -> [m_chunk, n] bf16,
+ *               contiguous (rank s's chunk: &out_s[c * m_chunk * n])
+ * residual      [m_chunk, n] bf16 contiguous
+ * gamma         [n] bf16
+ * eps           >= 0, finite (e.g. 1e-6)
+ * y             [m_chunk, n] bf16; must not overlap any input or residual_out
+ * residual_out  [m_chunk, n] bf16; may be exactly residual (in place), must
+ *               not otherwise overlap an input
+ *
+ * RPL_ERR_NULL        partials or gamma is NULL, or m_chunk > 0 and residual,
+ *                     y, residual_out or one of partials[0..tp-1] is NULL
+ *                     (entries are read only for tp <= RPL_MAX_TP)
+ * RPL_ERR_INVALID     tp < 1, m_chunk < 0, n < 1, eps < 0 or not finite,
+ *                     y overlaps an input or residual_out, residual_out
+ *                     partially overlaps residual or overlaps another input
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; n not a multiple of 8; n > 16384;
+ *                     any pointer not 16-byte aligned; m_chunk >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_reduce_chunk_rmsnorm(const rpl_bf16 *const *partials, int32_t tp,
+                                    int64_t m_chunk, int64_t n,
+                                    const rpl_bf16 *residual,
+                                    const rpl_bf16 *gamma, float eps,
+                                    rpl_bf16 *y, rpl_bf16 *residual_out,
+                                    void *stream);
+
+/*
+ * rpl_w8a8_partial -- the w8a8 (dynamic-quant) rank partial.
+ *
+ * [FC1] review thread (w8a8_dynamic quant matmul): int8 activations carry a
+ * per-token scale, int8 weights a per-output-channel weight_scale, which is
+ * required; the integer product is dequantised.
+ *
+ *   acc[r, j] = sum_{k < K} xq[r, k] * wq[j, k]                   (exact int32)
+ *   out[r, j] = bf16_rne( (float(acc[r, j]) * x_scale[r]) * w_scale[j] )
+ * with int -> fp32 nearest-even and two fp32 multiplies in exactly this order
+ * (no fused multiply-add); rows m <= r < M_pad give acc = 0 and out = 0.
+ * The caller guarantees |acc| < 2^31 (always true for k < 131072; with codes
+ * in [-127, 127] for k <= 133143).
+ *
+ * xq       [m, k] int8, row stride ldx >= k
+ * x_scale  [m] fp32 per-token scale
+ * wq       [n, k] int8, row stride ldw >= k
+ * w_scale  [n] fp32 per-channel scale (required)
+ * out      [M_pad, n] bf16 contiguous, chunk layout as rpl_partial
+ * acc      optional [M_pad, n] int32 contiguous (NULL = not stored)
+ * out and acc must not overlap each other or any input.
+ *
+ * RPL_ERR_NULL        wq or w_scale is NULL, or m > 0 and xq, x_scale or out
+ *                     is NULL
+ * RPL_ERR_INVALID     m < 0, n < 1, k < 1, tp < 1, ldx < k, ldw < k, overlaps
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; k, ldx or ldw not a multiple of 16;
+ *                     n not a multiple of 8; xq, wq, out, acc not 16-byte
+ *                     aligned or scales not 4-byte aligned; m, n or k >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
+                            const int8_t *wq, int64_t ldw, const float *w_scale,
+                            rpl_bf16 *out, int32_t *acc,
+                            int64_t m, int64_t n, int64_t k, int32_t tp,
+                            void *stream);
+
+/* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
+const char *rpl_status_string(rpl_status s);
+
+/* Library ABI version: (major << 16) | minor.  Currently 1.0. */
+int32_t rpl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPL_H */

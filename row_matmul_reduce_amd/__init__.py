@@ -1,0 +1,198 @@
+"""row_matmul_reduce_amd -- row-parallel matmul + reduce on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``librpl.so`` (declared in
+``include/rpl.h``).  It only marshals arguments: it checks dtypes, devices
+and layouts of torch tensors, allocates outputs when none are given, and
+passes raw device pointers plus torch's current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback: if
+the library is missing, every call raises.
+
+    rpl_partial(x, w, tp)                      -> [M_pad, n] bf16 partial
+    rpl_reduce_chunk_rmsnorm(partials, residual, gamma, eps)
+                                               -> (y, residual_out)
+    rpl_w8a8_partial(xq, x_scale, wq, w_scale, tp, want_acc=False)
+                                               -> out (, acc)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librpl.so")
+
+RPL_OK, RPL_ERR_NULL, RPL_ERR_INVALID, RPL_ERR_UNSUPPORTED, RPL_ERR_LAUNCH = range(5)
+RPL_MAX_TP = 16
+
+_p, _i64, _i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+_lib = None
+
+
+class RplError(RuntimeError):
+    """A non-OK status from librpl."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {rpl_status_string(status)}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load librpl.so (built in-tree by ``python -m row_matmul_reduce_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"librpl.so is not built ({LIB_PATH}); run python -m row_matmul_reduce_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.rpl_partial.restype = ctypes.c_int
+        L.rpl_partial.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i32, _p]
+        L.rpl_reduce_chunk_rmsnorm.restype = ctypes.c_int
+        L.rpl_reduce_chunk_rmsnorm.argtypes = [_p, _i32, _i64, _i64, _p, _p, ctypes.c_float, _p, _p, _p]
+        L.rpl_w8a8_partial.restype = ctypes.c_int
+        L.rpl_w8a8_partial.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
+        L.rpl_status_string.restype = ctypes.c_char_p
+        L.rpl_status_string.argtypes = [ctypes.c_int]
+        L.rpl_version.restype = ctypes.c_int32
+        L.rpl_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def rpl_status_string(status: int) -> str:
+    return lib().rpl_status_string(int(status)).decode()
+
+
+def rpl_version() -> int:
+    return int(lib().rpl_version())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != RPL_OK:
+        raise RplError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name: str, dtype, ndim: int):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU (HIP) tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim}-D, got shape {tuple(t.shape)}")
+    if ndim == 2 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: rows must be contiguous (stride(1) == 1)")
+    if ndim == 1 and t.shape[0] > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _stream(t, stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(t.device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ld(t) -> int:
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def m_pad_of(m: int, tp: int) -> int:
+    return -(-m // tp) * tp
+
+
+def rpl_partial(x, w, tp: int, out=None, stream=None):
+    """One rank's bf16 partial, [M_pad, n] in reduce-scatter chunk layout."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(w, "w", torch.bfloat16, 2)
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError(f"x {tuple(x.shape)} and w {tuple(w.shape)} disagree on k")
+    mp = m_pad_of(m, tp) if tp >= 1 else m
+    if out is None:
+        out = torch.empty((mp, n), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (mp, n) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{mp}, {n}] tensor")
+    st = lib().rpl_partial(x.data_ptr(), _ld(x), w.data_ptr(), _ld(w), out.data_ptr(), m, n, k, tp,
+                           _stream(x, stream))
+    _check("rpl_partial", st)
+    return out
+
+
+def rpl_reduce_chunk_rmsnorm(partials, residual, gamma, eps: float, y=None, residual_out=None, stream=None):
+    """Sum of the tp chunk partials + residual, then RMSNorm -> (y, residual_out)."""
+    torch = _torch()
+    partials = list(partials)
+    if not partials:
+        raise ValueError("need at least one partial")
+    for i, p in enumerate(partials):
+        _dev(p, f"partials[{i}]", torch.bfloat16, 2)
+        if tuple(p.shape) != tuple(partials[0].shape) or not p.is_contiguous():
+            raise ValueError("partials must be contiguous and share one shape")
+    m_chunk, n = partials[0].shape
+    _dev(residual, "residual", torch.bfloat16, 2)
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    if tuple(residual.shape) != (m_chunk, n) or not residual.is_contiguous():
+        raise ValueError("residual must be a contiguous [m_chunk, n] tensor")
+    if gamma.shape[0] != n:
+        raise ValueError("gamma must have n entries")
+    if y is None:
+        y = torch.empty((m_chunk, n), dtype=torch.bfloat16, device=residual.device)
+    if residual_out is None:
+        residual_out = torch.empty((m_chunk, n), dtype=torch.bfloat16, device=residual.device)
+    for name, t in (("y", y), ("residual_out", residual_out)):
+        _dev(t, name, torch.bfloat16, 2)
+        if tuple(t.shape) != (m_chunk, n) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [m_chunk, n] tensor")
+    arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
+    st = lib().rpl_reduce_chunk_rmsnorm(ctypes.cast(arr, ctypes.c_void_p), len(partials), m_chunk, n,
+                                        residual.data_ptr(), gamma.data_ptr(), float(eps), y.data_ptr(),
+                                        residual_out.data_ptr(), _stream(residual, stream))
+    _check("rpl_reduce_chunk_rmsnorm", st)
+    return y, residual_out
+
+
+def rpl_w8a8_partial(xq, x_scale, wq, w_scale, tp: int, out=None, acc=None, want_acc: bool = False,
+                     stream=None):
+    """int8 x int8 rank partial, dequantised to bf16 [M_pad, n]; optionally the int32 accumulators."""
+    torch = _torch()
+    _dev(xq, "xq", torch.int8, 2)
+    _dev(wq, "wq", torch.int8, 2)
+    _dev(x_scale, "x_scale", torch.float32, 1)
+    _dev(w_scale, "w_scale", torch.float32, 1)
+    m, k = xq.shape
+    n = wq.shape[0]
+    if wq.shape[1] != k:
+        raise ValueError("xq and wq disagree on k")
+    if x_scale.shape[0] != m or w_scale.shape[0] != n:
+        raise ValueError("x_scale must have m entries and w_scale n entries")
+    mp = m_pad_of(m, tp) if tp >= 1 else m
+    if out is None:
+        out = torch.empty((mp, n), dtype=torch.bfloat16, device=xq.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (mp, n) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{mp}, {n}] tensor")
+    if acc is None and want_acc:
+        acc = torch.empty((mp, n), dtype=torch.int32, device=xq.device)
+    if acc is not None:
+        _dev(acc, "acc", torch.int32, 2)
+        if tuple(acc.shape) != (mp, n) or not acc.is_contiguous():
+            raise ValueError(f"acc must be a contiguous [{mp}, {n}] tensor")
+    st = lib().rpl_w8a8_partial(xq.data_ptr(), _ld(xq), x_scale.data_ptr(), wq.data_ptr(), _ld(wq),
+                                w_scale.data_ptr(), out.data_ptr(), None if acc is None else acc.data_ptr(),
+                                m, n, k, tp, _stream(xq, stream))
+    _check("rpl_w8a8_partial", st)
+    return (out, acc) if acc is not None else out
+
+
+__all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_status_string", "rpl_version",
+           "RplError", "lib", "m_pad_of", "LIB_PATH"]

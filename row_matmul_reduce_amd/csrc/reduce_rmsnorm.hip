@@ -1,0 +1,134 @@
+// reduce_rmsnorm.hip -- the receiving rank's epilogue on gfx950: sum of all
+// tensor-parallel partials for its token chunk, residual add, RMSNorm.
+//
+// What it computes (xLLM pull request #1890, "feat: add FlashComm1 and MMRS
+// fusion support for Qwen3.5 NPU", Summary and review thread: the
+// sequence-parallel reduction is a reduce-scatter over tokens and the residual
+// add + RMSNorm run on the local chunk; Dewu tech blog
+// "国产算力·昇腾 910C 大模型推理优化（下）：源码修改与算子优化", communication-
+// fusion section: after the cross-rank sum the residual is added, that sum is
+// the next residual, and RMSNorm takes the sum of squares, its reciprocal root
+// and the weighted product):
+//   h            = sum_s P_s[i, :] + residual[i, :]          (fp32 registers)
+//   residual_out = bf16(h)
+//   y            = bf16( gamma * h * rsqrt(mean(h^2) + eps) )
+//
+// HBM-bound: every byte is read or written once.  A row is owned by a team of
+// RW wavefronts; lane t of the team holds 16-byte chunks t, t + 64*RW, ... of
+// the row (CPL of them) in fp32 registers, so the row is read once, the sum of
+// squares is a wavefront butterfly (plus an LDS exchange between the team's
+// waves when RW > 1), and both outputs are written from registers.  The
+// residual is read before either output is written, so residual_out may be
+// the residual buffer itself.
+#include "rpl_device.h"
+#include "rpl_launch.h"
+
+namespace rpl {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int CPL, int RW>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
+reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t *__restrict__ residual,
+                      const uint16_t *__restrict__ gamma, float eps, uint16_t *y, uint16_t *residual_out) {
+    constexpr int ROWS = 4 / RW;  // rows per 256-thread workgroup
+    __shared__ float team_sum[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = blockIdx.x * ROWS + wave / RW;
+    const int t = (wave % RW) * 64 + lane;
+    const int nch = n >> 3;
+    const bool row_ok = row < m_chunk;  // RW > 1: the whole workgroup shares one row
+
+    float h[CPL][8];
+    const int64_t rbase = (int64_t)row * n;
+    if (row_ok) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = t + j * 64 * RW;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+            if (c < nch) {
+                for (int s = 0; s < tp; ++s) {
+                    const u32x4 v = ld16(P.p[s] + rbase + c * 8);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        h[j][2 * q] += bf16_lo(v[q]);
+                        h[j][2 * q + 1] += bf16_hi(v[q]);
+                    }
+                }
+                const u32x4 r = ld16(residual + rbase + c * 8);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    h[j][2 * q] += bf16_lo(r[q]);
+                    h[j][2 * q + 1] += bf16_hi(r[q]);
+                }
+            }
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += h[j][e] * h[j][e];
+    ss = wave_sum(ss);
+    if (RW > 1) {
+        if (lane == 0) team_sum[wave] = ss;
+        __syncthreads();
+        ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < RW; ++v) ss += team_sum[v];
+    }
+    if (!row_ok) return;
+    const float inv = rsqrtf(ss / (float)n + eps);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = t + j * 64 * RW;
+        if (c < nch) {
+            const u32x4 gv = ld16(gamma + c * 8);
+            u32x4 yo, ro;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float a = h[j][2 * q], b = h[j][2 * q + 1];
+                ro[q] = pack_bf16x2(a, b);
+                yo[q] = pack_bf16x2(bf16_lo(gv[q]) * (a * inv), bf16_hi(gv[q]) * (b * inv));
+            }
+            st16(residual_out + rbase + c * 8, ro);
+            st16(y + rbase + c * 8, yo);
+        }
+    }
+}
+
+template <int CPL, int RW>
+static hipError_t launch_rr(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
+                            const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
+    constexpr int ROWS = 4 / RW;
+    hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPL, RW>), dim3((m_chunk + ROWS - 1) / ROWS), dim3(256), 0, st, p, tp,
+                       m_chunk, n, residual, gamma, eps, y, ro);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
+                                 const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
+    const int nch = n / 8;
+    if (nch <= 64 * 12) {  // one wavefront per row, up to 12 chunks (96 values) per lane
+        switch ((nch + 63) / 64) {
+#define RR1(C) \
+    case C: return launch_rr<C, 1>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
+            RR1(1) RR1(2) RR1(3) RR1(4) RR1(5) RR1(6) RR1(7) RR1(8) RR1(9) RR1(10) RR1(11) RR1(12)
+#undef RR1
+        }
+    }
+    switch ((nch + 255) / 256) {  // four wavefronts per row (n <= 16384)
+#define RR4(C) \
+    case C: return launch_rr<C, 4>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
+        RR4(1) RR4(2) RR4(3) RR4(4) RR4(5) RR4(6) RR4(7) RR4(8)
+#undef RR4
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rpl

@@ -1,0 +1,142 @@
+// rpl_api.cpp -- the C ABI of librpl: host-side argument checks, then launch.
+//
+// Every check runs on the host, in the order of the status codes (NULL, then
+// INVALID, then UNSUPPORTED), before any HIP call, so a rejected call touches
+// neither the device nor the outputs.  This mirrors the fallback convention of
+// the pages' fused operators: xLLM pull request #1890, "feat: add FlashComm1 and
+// MMRS fusion support for Qwen3.5 NPU" ("MMRS Integration": unsupported inputs
+// return nothing and the caller keeps its unfused matmul + reduce path), and the
+// Dewu 910C blog's fused o_proj operator (communication-fusion section: a guard
+// declines unsupported shapes so the unfused composition runs instead).
+#include <cmath>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/rpl.h"
+#include "rpl_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p + bytes) overlap?
+bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+// Saturating arithmetic on non-negative sizes, so absurd arguments cannot overflow
+// before they are rejected.
+int64_t smul(int64_t a, int64_t b) {
+    const __int128 r = (__int128)a * b;
+    return r > INT64_MAX ? INT64_MAX : (int64_t)r;
+}
+int64_t sadd(int64_t a, int64_t b) { return a > INT64_MAX - b ? INT64_MAX : a + b; }
+
+// Bytes spanned by a row-major [rows, cols] matrix with row stride ld elements.
+int64_t span(int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+    return rows <= 0 ? 0 : smul(sadd(smul(rows - 1, ld), cols), esize);
+}
+
+int64_t padded_rows(int64_t m, int32_t tp) { return m > kMaxDim ? m : (m + tp - 1) / tp * tp; }
+
+rpl_status launch_status(hipError_t e) { return e == hipSuccess ? RPL_OK : RPL_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+rpl_status rpl_partial(const rpl_bf16 *x, int64_t ldx, const rpl_bf16 *w, int64_t ldw, rpl_bf16 *out, int64_t m,
+                       int64_t n, int64_t k, int32_t tp, void *stream) {
+    if (!w || (m != 0 && (!x || !out))) return RPL_ERR_NULL;
+    if (m < 0 || n < 1 || k < 1 || tp < 1 || ldx < k || ldw < k) return RPL_ERR_INVALID;
+    const int64_t m_pad = padded_rows(m, tp);
+    const int64_t out_bytes = span(m_pad, n, n, 2);
+    if (overlap(out, out_bytes, x, span(m, k, ldx, 2)) || overlap(out, out_bytes, w, span(n, k, ldw, 2)))
+        return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || k % 8 || n % 8 || ldx % 8 || ldw % 8) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16)) return RPL_ERR_UNSUPPORTED;
+    if (m_pad > kMaxDim || n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    return launch_status(rpl::launch_partial_bf16(x, ldx, w, ldw, out, (int)m, (int)m_pad, (int)n, (int)k,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_reduce_chunk_rmsnorm(const rpl_bf16 *const *partials, int32_t tp, int64_t m_chunk, int64_t n,
+                                    const rpl_bf16 *residual, const rpl_bf16 *gamma, float eps, rpl_bf16 *y,
+                                    rpl_bf16 *residual_out, void *stream) {
+    if (!partials || !gamma) return RPL_ERR_NULL;
+    if (m_chunk != 0) {
+        if (!residual || !y || !residual_out) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!partials[s]) return RPL_ERR_NULL;
+    }
+    if (tp < 1 || m_chunk < 0 || n < 1 || !(eps >= 0.0f) || !std::isfinite(eps)) return RPL_ERR_INVALID;
+    const int64_t mat = span(m_chunk, n, n, 2);
+    const int64_t gbytes = span(1, n, n, 2);
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    // y must not overlap any input nor residual_out.
+    if (overlap(y, mat, residual, mat) || overlap(y, mat, gamma, gbytes) || overlap(y, mat, residual_out, mat))
+        return RPL_ERR_INVALID;
+    for (int s = 0; s < np; ++s)
+        if (overlap(y, mat, partials[s], mat)) return RPL_ERR_INVALID;
+    // residual_out may be exactly residual, but must not otherwise overlap an input.
+    if (residual_out != residual && overlap(residual_out, mat, residual, mat)) return RPL_ERR_INVALID;
+    if (overlap(residual_out, mat, gamma, gbytes)) return RPL_ERR_INVALID;
+    for (int s = 0; s < np; ++s)
+        if (overlap(residual_out, mat, partials[s], mat)) return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || n % 8 || n > 16384) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(y, 16) || !aligned(residual_out, 16))
+        return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp; ++s)
+        if (!aligned(partials[s], 16)) return RPL_ERR_UNSUPPORTED;
+    if (m_chunk > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m_chunk == 0) return RPL_OK;
+    rpl::PartialPtrs p{};
+    for (int s = 0; s < tp; ++s) p.p[s] = partials[s];
+    return launch_status(rpl::launch_reduce_rmsnorm(p, tp, (int)m_chunk, (int)n, residual, gamma, eps, y,
+                                                    residual_out, static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale, const int8_t *wq, int64_t ldw,
+                            const float *w_scale, rpl_bf16 *out, int32_t *acc, int64_t m, int64_t n, int64_t k,
+                            int32_t tp, void *stream) {
+    if (!wq || !w_scale || (m != 0 && (!xq || !x_scale || !out))) return RPL_ERR_NULL;
+    if (m < 0 || n < 1 || k < 1 || tp < 1 || ldx < k || ldw < k) return RPL_ERR_INVALID;
+    const int64_t m_pad = padded_rows(m, tp);
+    const int64_t ob = span(m_pad, n, n, 2), ab = span(m_pad, n, n, 4);
+    const int64_t xb = span(m, k, ldx, 1), wb = span(n, k, ldw, 1);
+    if (overlap(out, ob, xq, xb) || overlap(out, ob, wq, wb) || overlap(out, ob, x_scale, span(1, m, m, 4)) ||
+        overlap(out, ob, w_scale, span(1, n, n, 4)))
+        return RPL_ERR_INVALID;
+    if (acc && (overlap(acc, ab, out, ob) || overlap(acc, ab, xq, xb) || overlap(acc, ab, wq, wb) ||
+                overlap(acc, ab, x_scale, span(1, m, m, 4)) || overlap(acc, ab, w_scale, span(1, n, n, 4))))
+        return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || k % 16 || ldx % 16 || ldw % 16 || n % 8) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(out, 16) || (acc && !aligned(acc, 16)) ||
+        !aligned(x_scale, 4) || !aligned(w_scale, 4))
+        return RPL_ERR_UNSUPPORTED;
+    if (m_pad > kMaxDim || n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    return launch_status(rpl::launch_partial_w8a8(xq, ldx, x_scale, wq, ldw, w_scale, out, acc, (int)m, (int)m_pad,
+                                                  (int)n, (int)k, static_cast<hipStream_t>(stream)));
+}
+
+const char *rpl_status_string(rpl_status s) {
+    switch (s) {
+        case RPL_OK: return "RPL_OK";
+        case RPL_ERR_NULL: return "RPL_ERR_NULL";
+        case RPL_ERR_INVALID: return "RPL_ERR_INVALID";
+        case RPL_ERR_UNSUPPORTED: return "RPL_ERR_UNSUPPORTED";
+        case RPL_ERR_LAUNCH: return "RPL_ERR_LAUNCH";
+    }
+    return "unknown";
+}
+
+int32_t rpl_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// rpl_device.h -- device-side helpers shared by the gfx950 kernels of librpl.
+//
+// Vector types for 16-byte global/LDS traffic and for the MFMA operands, and
+// bfloat16 <-> fp32 conversions.  fp32 -> bf16 uses the compiler's __bf16
+// conversion, which gfx950 lowers to v_cvt_pk_bf16_f32 (round to nearest,
+// ties to even); bf16 -> fp32 is exact (a shift).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16x2 (low half = a), nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    bf16x2 h = __builtin_convertvector(v, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Packed bf16 pair -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xFFFF0000u); }
+
+// 16-byte global load / store (the address must be 16-byte aligned).
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+__device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
+
+}  // namespace rpl

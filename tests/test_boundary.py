@@ -1,0 +1,215 @@
+"""CPU-only tests of the C ABI boundary (librpl.so), no GPU needed.
+
+The library must load without a GPU and export every function that
+include/rpl.h declares.  Every argument check runs on the host before any HIP
+call, so calls that fail validation are safe to make here; they must return
+the documented status and leave the output buffers untouched.  Buffers here
+are host memory standing in for device memory: a rejected call must not
+touch them.  No call in this file reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import row_matmul_reduce_amd as rpl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rpl.h")
+
+OK, NULL, INVALID, UNSUP = rpl.RPL_OK, rpl.RPL_ERR_NULL, rpl.RPL_ERR_INVALID, rpl.RPL_ERR_UNSUPPORTED
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rpl_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_status_string", "rpl_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = rpl.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in rpl.h but not exported"
+    # and exports no other rpl_ function (nm on the built object)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rpl.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if re.search(r" T rpl_", ln)})
+    assert exported == declared_functions()
+
+
+def test_status_strings_and_version():
+    assert [rpl.rpl_status_string(s) for s in range(5)] == [
+        "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
+    assert rpl.rpl_status_string(99) == "unknown"
+    assert rpl.rpl_version() == (1 << 16)
+
+
+class Buf:
+    """16-byte aligned host buffer filled with a sentinel; reports whether it changed."""
+
+    def __init__(self, nbytes, offset=0):
+        # generous slack so that spans of strided test shapes stay inside the buffer
+        self.raw = np.full(2 * nbytes + 4096, 0xA5, dtype=np.uint8)
+        base = self.raw.ctypes.data
+        self.start = (-base) % 16 + offset
+        self.ptr = base + self.start
+
+    def untouched(self):
+        return bool(np.all(self.raw == 0xA5))
+
+
+def partial(x, ldx, w, ldw, out, m, n, k, tp):
+    return rpl.lib().rpl_partial(x, ldx, w, ldw, out, m, n, k, tp, None)
+
+
+def test_partial_validation():
+    m, n, k, tp = 6, 16, 32, 2
+    X, W, O = Buf(m * k * 2), Buf(n * k * 2), Buf(m * n * 2)
+    x, w, o = X.ptr, W.ptr, O.ptr
+    cases = [
+        ((x, k, None, k, o, m, n, k, tp), NULL),
+        ((None, k, w, k, o, m, n, k, tp), NULL),
+        ((x, k, w, k, None, m, n, k, tp), NULL),
+        ((x, k, w, k, o, -1, n, k, tp), INVALID),
+        ((x, k, w, k, o, m, 0, k, tp), INVALID),
+        ((x, k, w, k, o, m, n, 0, tp), INVALID),
+        ((x, k, w, k, o, m, n, k, 0), INVALID),
+        ((x, k - 8, w, k, o, m, n, k, tp), INVALID),
+        ((x, k, w, k - 8, o, m, n, k, tp), INVALID),
+        ((x, k, w, k, x + 16, m, n, k, tp), INVALID),            # out overlaps x
+        ((x, k, w, k, w, m, n, k, tp), INVALID),                 # out overlaps w
+        ((x, k, w, k, o, m, n, k, 17), UNSUP),
+        ((x, 40, w, 40, o, m, n, 36, tp), UNSUP),                 # k % 8
+        ((x, k, w, k, o, m, 20, k, tp), UNSUP),                   # n % 8
+        ((x, 36, w, k, o, m, n, k, tp), UNSUP),                   # ldx % 8
+        ((x + 2, k, w, k, o, m, n, k, tp), UNSUP),                # misaligned x
+        ((x, k, w + 8, k, o, m, n, k, tp), UNSUP),                # misaligned w
+        ((x, k, w, k, o + 4, m, n, k, tp), UNSUP),                # misaligned out
+        # too many rows (far-apart fake addresses: never dereferenced, no overlap)
+        ((1 << 44, k, 1 << 45, k, 1 << 46, 1 << 31, n, k, tp), UNSUP),
+    ]
+    for args, want in cases:
+        assert partial(*args) == want, args
+    assert X.untouched() and W.untouched() and O.untouched()
+    # empty batch: OK without touching anything (x and out may be NULL)
+    assert partial(None, k, w, k, None, 0, n, k, tp) == OK
+    assert partial(x, k, w, k, o, 0, n, k, tp) == OK
+    assert X.untouched() and W.untouched() and O.untouched()
+
+
+def reduce_call(parts, tp, mc, n, res, gam, eps, y, ro):
+    arr = None if parts is None else (ctypes.c_void_p * len(parts))(*parts)
+    return rpl.lib().rpl_reduce_chunk_rmsnorm(None if arr is None else ctypes.cast(arr, ctypes.c_void_p), tp, mc,
+                                              n, res, gam, eps, y, ro, None)
+
+
+def test_reduce_validation():
+    tp, mc, n = 2, 4, 64
+    mat = mc * n * 2
+    P0, P1, R, G, Y, RO = Buf(mat), Buf(mat), Buf(mat), Buf(n * 2), Buf(mat), Buf(mat)
+    p = [P0.ptr, P1.ptr]
+    r, g, y, ro = R.ptr, G.ptr, Y.ptr, RO.ptr
+    cases = [
+        ((None, tp, mc, n, r, g, 1e-6, y, ro), NULL),
+        (([p[0], None], tp, mc, n, r, g, 1e-6, y, ro), NULL),
+        ((p, tp, mc, n, None, g, 1e-6, y, ro), NULL),
+        ((p, tp, mc, n, r, None, 1e-6, y, ro), NULL),
+        ((p, tp, mc, n, r, g, 1e-6, None, ro), NULL),
+        ((p, tp, mc, n, r, g, 1e-6, y, None), NULL),
+        ((p, 0, mc, n, r, g, 1e-6, y, ro), INVALID),
+        ((p, tp, -1, n, r, g, 1e-6, y, ro), INVALID),
+        ((p, tp, mc, 0, r, g, 1e-6, y, ro), INVALID),
+        ((p, tp, mc, n, r, g, -1e-6, y, ro), INVALID),
+        ((p, tp, mc, n, r, g, float("nan"), y, ro), INVALID),
+        ((p, tp, mc, n, r, g, float("inf"), y, ro), INVALID),
+        ((p, tp, mc, n, r, g, 1e-6, r, ro), INVALID),             # y aliases residual
+        ((p, tp, mc, n, r, g, 1e-6, p[1], ro), INVALID),          # y aliases a partial
+        ((p, tp, mc, n, r, g, 1e-6, y, y), INVALID),              # y aliases residual_out
+        ((p, tp, mc, n, r, g, 1e-6, g, ro), INVALID),             # y overlaps gamma
+        ((p, tp, mc, n, r, g, 1e-6, y, r + 16), INVALID),         # residual_out partially overlaps residual
+        ((p, tp, mc, n, r, g, 1e-6, y, p[0]), INVALID),           # residual_out aliases a partial
+        ((p * 9, 18, mc, n, r, g, 1e-6, y, ro), UNSUP),           # tp > 16
+        ((p, tp, mc, 60, r, g, 1e-6, y, ro), UNSUP),              # n % 8
+        # n > 16384 (far-apart fake addresses: never dereferenced, no overlap)
+        (([1 << 40, 1 << 41], tp, mc, 16392, 1 << 42, 1 << 43, 1e-6, 1 << 44, 1 << 45), UNSUP),
+        (([p[0] + 8, p[1]], tp, mc, n, r, g, 1e-6, y, ro), UNSUP),
+        ((p, tp, mc, n, r, g + 2, 1e-6, y, ro), UNSUP),
+        ((p, tp, mc, n, r, g, 1e-6, y + 8, ro), UNSUP),
+    ]
+    for args, want in cases:
+        assert reduce_call(*args) == want, args
+    for b in (P0, P1, R, G, Y, RO):
+        assert b.untouched()
+    assert reduce_call([None, None], tp, 0, n, None, g, 1e-6, None, None) == OK
+    for b in (P0, P1, R, G, Y, RO):
+        assert b.untouched()
+
+
+def w8a8_call(xq, ldx, sx, wq, ldw, sw, out, acc, m, n, k, tp):
+    return rpl.lib().rpl_w8a8_partial(xq, ldx, sx, wq, ldw, sw, out, acc, m, n, k, tp, None)
+
+
+def test_w8a8_validation():
+    m, n, k, tp = 6, 16, 64, 2
+    XQ, SX, WQ, SW, O, A = Buf(m * k), Buf(m * 4), Buf(n * k), Buf(n * 4), Buf(m * n * 2), Buf(m * n * 4)
+    xq, sx, wq, sw, o, a = XQ.ptr, SX.ptr, WQ.ptr, SW.ptr, O.ptr, A.ptr
+    cases = [
+        ((None, k, sx, wq, k, sw, o, a, m, n, k, tp), NULL),
+        ((xq, k, None, wq, k, sw, o, a, m, n, k, tp), NULL),
+        ((xq, k, sx, None, k, sw, o, a, m, n, k, tp), NULL),
+        ((xq, k, sx, wq, k, None, o, a, m, n, k, tp), NULL),       # weight_scale is required
+        ((xq, k, sx, wq, k, sw, None, a, m, n, k, tp), NULL),
+        ((xq, k, sx, wq, k, sw, o, a, -2, n, k, tp), INVALID),
+        ((xq, k, sx, wq, k, sw, o, a, m, n, k, 0), INVALID),
+        ((xq, 48, sx, wq, k, sw, o, a, m, n, k, tp), INVALID),
+        ((xq, k, sx, wq, k, sw, o, o, m, n, k, tp), INVALID),      # acc aliases out
+        ((xq, k, sx, wq, k, sw, xq, a, m, n, k, tp), INVALID),     # out aliases xq
+        ((xq, k, sx, wq, k, sw, o, sw, m, n, k, tp), INVALID),     # acc overlaps w_scale
+        ((xq, 80, sx, wq, 80, sw, o, a, m, n, 72, tp), UNSUP),     # k % 16
+        ((xq, 72, sx, wq, k, sw, o, a, m, n, k, tp), UNSUP),       # ldx % 16
+        ((xq, k, sx, wq, k, sw, o, a, m, 12, k, tp), UNSUP),       # n % 8
+        ((xq + 8, k, sx, wq, k, sw, o, a, m, n, k, tp), UNSUP),
+        ((xq, k, sx + 2, wq, k, sw, o, a, m, n, k, tp), UNSUP),
+        ((xq, k, sx, wq, k, sw, o, a + 4, m, n, k, tp), UNSUP),
+        ((xq, k, sx, wq, k, sw, o, a, m, n, k, 32), UNSUP),
+    ]
+    for args, want in cases:
+        assert w8a8_call(*args) == want, args
+    for b in (XQ, SX, WQ, SW, O, A):
+        assert b.untouched()
+    assert w8a8_call(None, k, None, wq, k, sw, None, None, 0, n, k, tp) == OK
+    for b in (XQ, SX, WQ, SW, O, A):
+        assert b.untouched()
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding refuses CPU tensors before anything reaches the library."""
+    import torch
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    w = torch.zeros(8, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        rpl.rpl_partial(x, w, 2)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(rpl, "_lib", None)
+    monkeypatch.setattr(rpl, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        rpl.lib()
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "row_matmul_reduce_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b|rpl_oracle|\borc_", text, flags=re.M), f
