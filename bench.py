@@ -1,21 +1,25 @@
 """Benchmark of the row-parallel matmul + reduce hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|decode|long_prefill]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long_prefill|w8a8|decode|tiny]
 
-One step is one pass of the whole path for one tensor-parallel rank, on
-synthetic inputs already resident in HBM:
-  1. rpl_partial               the rank's bf16 partial over its K-shard, all
-                               M tokens, written as reduce-scatter chunks;
-  2. rpl_w8a8_partial          the w8a8 (int8) partial of the same shape
-                               (skipped for workloads without a w8a8 variant);
-  3. rpl_reduce_chunk_rmsnorm  the received chunk: own chunk partial + the
-                               peers' chunk partials (arrived data, produced
-                               before timing) -> residual add -> RMSNorm.
-The default workload is the 7B-class prefill down_proj share (M=4096,
-K_full=18944 over TP=2, N=3584) with its w8a8 twin.  The JSON line reports the
-step's algorithmic tera-ops per second (bf16 FLOP + int8 OP), per-kernel
-times from HIP events on the launch stream, the roofline of the dominant
-kernel, and the CPU oracle timed on a bounded sample of the same work.
+One step is one pass of the path for one tensor-parallel rank, on synthetic
+inputs already resident in HBM:
+  1. the rank's partial over its K-shard (rpl_partial in bf16, or
+     rpl_w8a8_partial for the w8a8 path), all M tokens, written as
+     reduce-scatter token chunks;
+  2. rpl_reduce_chunk_rmsnorm on the chunk the rank receives: its own chunk
+     partial + the peers' chunk partials (data that arrives from the other
+     ranks, produced before timing) -> residual add -> RMSNorm.
+A model layer runs the bf16 or the w8a8 partial, not both, so each precision is
+its own path.  The default run times the bf16 prefill down_proj share
+(M=4096, K_full=18944 over TP=2, N=3584) as the main step, and in the same run
+the w8a8 twin, the decode o_proj share and the TP=8 long-prefill share as side
+steps.  Every step cycles through several copies of its inputs (more than
+twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
+
+The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
+from HIP events on the launch stream, the roofline of the dominant kernel, and
+the CPU oracle timed on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -35,7 +39,9 @@ METRIC = "TFLOP/s and % of MFMA peak (prefill); HBM GB/s % peak (decode)"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_I8_TOPS = 5033.2       # dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E
+MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ["gemm_nt.h", "gemm_bf16.hip", "gemm_w8a8.hip", "reduce_rmsnorm.hip", "rpl_device.h"]
+WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5}
 
 
 def log(*a):
@@ -62,31 +68,152 @@ def load_traffic(kernel_key: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def to_dev_bf16(a, torch):
-    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+class Path:
+    """One rank's step (partial + received-chunk reduce/RMSNorm) on several input sets."""
+
+    def __init__(self, wl, torch, rpl, copies: int):
+        from row_matmul_reduce_amd import synth
+        self.wl, self.torch, self.rpl = wl, torch, rpl
+        self.w8 = wl.kind == "w8a8"
+        t0 = time.perf_counter()
+        mc = wl.m_chunk
+        dev = torch.device("cuda")
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        base = {"res": bf(synth.residual_chunk(wl)), "gam": bf(synth.gamma(wl))}
+        if self.w8:
+            xq, sx, wq, sw = synth.w8a8_inputs(wl, shard=0)
+            base.update(xq=up(xq), sx=up(sx), wq=up(wq), sw=up(sw))
+            peers = []
+            for s in range(1, wl.tp):
+                pq, psx, pwq, psw = synth.w8a8_inputs(wl, rows=mc, shard=s)
+                peers.append(rpl.rpl_w8a8_partial(up(pq), up(psx), up(pwq), up(psw), 1))
+        else:
+            base.update(x=bf(synth.x_shard(wl, 0)), w=bf(synth.w_shard(wl, 0)))
+            peers = [rpl.rpl_partial(bf(synth.x_shard(wl, s, rows=mc)), bf(synth.w_shard(wl, s)), 1)
+                     for s in range(1, wl.tp)]
+        base["peers"] = peers  # received chunk partials (bf16), produced before timing
+        self.set_bytes = sum(t.numel() * t.element_size() for v in base.values()
+                             for t in (v if isinstance(v, list) else [v]))
+        if copies <= 0:
+            copies = max(3, -(-(2 * MALL_BYTES + 1) // self.set_bytes) + 1)
+        self.sets = [base] + [{k: ([t.clone() for t in v] if isinstance(v, list) else v.clone())
+                               for k, v in base.items()} for _ in range(copies - 1)]
+        self.p = torch.empty((wl.m_pad, wl.n), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
+        self.ro = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
+        self.names = ["partial_w8a8" if self.w8 else "partial_bf16", "reduce_rmsnorm"]
+        torch.cuda.synchronize()
+        log(f"{wl.name}: inputs ready in {time.perf_counter() - t0:.1f} s, {len(self.sets)} copies x "
+            f"{self.set_bytes / 1e6:.0f} MB")
+
+    def partial(self, d):
+        if self.w8:
+            self.rpl.rpl_w8a8_partial(d["xq"], d["sx"], d["wq"], d["sw"], self.wl.tp, out=self.p)
+        else:
+            self.rpl.rpl_partial(d["x"], d["w"], self.wl.tp, out=self.p)
+
+    def reduce(self, d):
+        self.rpl.rpl_reduce_chunk_rmsnorm([self.p[:self.wl.m_chunk]] + d["peers"], d["res"], d["gam"],
+                                          self.wl.eps, y=self.y, residual_out=self.ro)
+
+    def step(self, i, evs=None):
+        d = self.sets[i % len(self.sets)]
+        if evs is not None:
+            evs[0][0].record()
+        self.partial(d)
+        if evs is not None:
+            evs[0][1].record()
+            evs[1][0].record()
+        self.reduce(d)
+        if evs is not None:
+            evs[1][1].record()
+
+    def run_graphs(self, steps: int, warmup: int):
+        """Small (decode) paths: the host launch cost exceeds the kernels, so time HIP graphs
+        that hold `steps` back-to-back launches; each replay runs them without host gaps."""
+        torch = self.torch
+        for i in range(max(warmup, len(self.sets))):
+            self.step(i)
+        torch.cuda.synchronize()
+
+        def capture(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    fn(self.sets[i % len(self.sets)], i)
+            g.replay()
+            torch.cuda.synchronize()
+            return g
+
+        def per_launch_us(g):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / steps
+
+        g_step = capture(lambda d, i: self.step(i))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g_step.replay()          # exactly `steps` steps
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = {self.names[0]: per_launch_us(capture(lambda d, i: self.partial(d))),
+                self.names[1]: per_launch_us(capture(lambda d, i: self.reduce(d)))}
+        return wall * 1e3 / steps, kern, kern[self.names[0]]
+
+    def run(self, steps: int, warmup: int):
+        """Time `steps` steps after `warmup`: wall ms per step, per-kernel HIP event means (us),
+        and the back-to-back launch period of the partial alone (us; includes launch gaps)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in self.names]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = {nm: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
+                for j, nm in enumerate(self.names)}
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            self.partial(self.sets[i % len(self.sets)])
+        b.record()
+        torch.cuda.synchronize()
+        period = a.elapsed_time(b) * 1e3 / steps
+        return wall * 1e3 / steps, kern, period
+
+    def kernels_report(self, kern, period):
+        wl = self.wl
+        pn, rn = self.names
+        flop, pbytes, rbytes = wl.gemm_flops(), wl.partial_bytes(), wl.reduce_bytes()
+        pu = kern[pn]
+        peak = PEAK_I8_TOPS if self.w8 else PEAK_BF16_TFLOPS
+        rate = flop / (pu * 1e-6) / 1e12
+        rep = {pn: {"us": pu, "back_to_back_period_us": period, "flop": flop,
+                    ("TOP/s" if self.w8 else "TFLOP/s"): rate, "frac_mfma_peak": rate / peak,
+                    "bytes": pbytes, "GB/s": pbytes / (pu * 1e-6) / 1e9}}
+        if self.w8:
+            rep[pn]["frac_bf16_peak_figure"] = rate / PEAK_BF16_TFLOPS
+        rep[pn]["frac_hbm"] = rep[pn]["GB/s"] / PEAK_HBM_GBS
+        ru = kern[rn]
+        rep[rn] = {"us": ru, "bytes": rbytes, "GB/s": rbytes / (ru * 1e-6) / 1e9}
+        rep[rn]["frac_hbm"] = rep[rn]["GB/s"] / PEAK_HBM_GBS
+        return rep
 
 
-def build_inputs(wl, w8, torch):
-    from row_matmul_reduce_amd import synth
-    t0 = time.perf_counter()
-    mc = wl.m_chunk
-    d = {
-        "x0": to_dev_bf16(synth.x_shard(wl, 0), torch),
-        "w0": to_dev_bf16(synth.w_shard(wl, 0), torch),
-        "res": to_dev_bf16(synth.residual_chunk(wl), torch),
-        "gam": to_dev_bf16(synth.gamma(wl), torch),
-        "peer_x": [to_dev_bf16(synth.x_shard(wl, s, rows=mc), torch) for s in range(1, wl.tp)],
-        "peer_w": [to_dev_bf16(synth.w_shard(wl, s), torch) for s in range(1, wl.tp)],
-    }
-    if w8 is not None:
-        xq, sx, wq, sw = synth.w8a8_inputs(w8)
-        d.update(xq=torch.from_numpy(xq).cuda(), sx=torch.from_numpy(sx).cuda(),
-                 wq=torch.from_numpy(wq).cuda(), sw=torch.from_numpy(sw).cuda())
-    log(f"inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
-    return d
-
-
-def cpu_baseline(wl, w8, budget_s: float):
+def cpu_baseline(wl, budget_s: float):
     """The CPU oracle on the first R token rows of the same step (R sized to the time budget)."""
     import oracle
     from row_matmul_reduce_amd import synth
@@ -95,51 +222,24 @@ def cpu_baseline(wl, w8, budget_s: float):
     x0, w0 = synth.x_shard(wl, 0, rows=mc), synth.w_shard(wl, 0)
     peers = [(synth.x_shard(wl, s, rows=mc), synth.w_shard(wl, s)) for s in range(1, wl.tp)]
     res, gam = synth.residual_chunk(wl), synth.gamma(wl)
-    if w8 is not None:
-        xq, sx, wq, sw = synth.w8a8_inputs(w8, rows=mc)
 
     def run(rows):
         r = np.arange(rows, dtype=np.int64)
         peer_parts = [oracle.partial_rows(px, pw, mc, rows=r) for px, pw in peers]  # arrived data: untimed
         t = time.perf_counter()
         own = oracle.partial_rows(x0, w0, wl.m, rows=r, tp=wl.tp)
-        if w8 is not None:
-            oracle.w8a8_rows(xq, sx, wq, sw, w8.m, rows=r, tp=w8.tp)
         oracle.reduce_chunk_rmsnorm([own] + peer_parts, res[:rows], gam, wl.eps)
         return time.perf_counter() - t
 
-    pilot_rows = 8
-    tp_ = run(pilot_rows)
-    rows = int(min(mc, max(pilot_rows, budget_s / max(tp_, 1e-9) * pilot_rows)))
+    pilot = 8
+    t_pilot = run(pilot)
+    rows = int(min(mc, max(pilot, budget_s / max(t_pilot, 1e-9) * pilot)))
     dt = run(rows)
-    ops = 2.0 * rows * wl.n * wl.k_shard * (2 if w8 is not None else 1)
-    return {"value": ops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {wl.m} token rows of the step (bf16 partial"
-                      f"{' + w8a8 partial' if w8 is not None else ''} + chunk reduce/RMSNorm), "
-                      f"fp64 C oracle, {dt:.1f} s"}
-
-
-def time_decode(torch, rpl, steps: int, copies: int):
-    """Decode o_proj partial (M=8) with the weight rotated over `copies` buffers (defeats the 256 MB MALL)."""
-    from row_matmul_reduce_amd import synth
-    wl = synth.WORKLOADS[2]
-    x = to_dev_bf16(synth.x_shard(wl, 0), torch)
-    w = to_dev_bf16(synth.w_shard(wl, 0), torch)
-    ws = [w] + [w.clone() for _ in range(copies - 1)]
-    out = torch.empty((wl.m_pad, wl.n), dtype=torch.bfloat16, device="cuda")
-    for i in range(copies):
-        rpl.rpl_partial(x, ws[i], wl.tp, out=out)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record()
-        rpl.rpl_partial(x, ws[i % copies], wl.tp, out=out)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
-    gbs = wl.partial_bytes() / (us * 1e-6) / 1e9
-    return {"workload": wl.name, "partial_us": us, "bytes": wl.partial_bytes(), "GB/s": gbs,
-            "frac_hbm": gbs / PEAK_HBM_GBS, "weight_copies_rotated": copies}
+    flop = 2.0 * rows * wl.n * wl.k_shard
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the step restricted to the first {rows} of {wl.m} token rows (partial rows + "
+                      f"chunk reduce/RMSNorm of those rows), fp64 C oracle with {threads} OpenMP threads, "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -147,15 +247,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "long_prefill", "tiny"])
+    ap.add_argument("--workload", default="prefill", choices=list(WORKLOAD_IDS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode o_proj side measurement")
+    ap.add_argument("--no-side", action="store_true", help="skip the side paths (w8a8, decode, long prefill)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="input sets cycled through (0: enough to exceed twice the 256 MB MALL)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this path is single-GPU (the cross-GPU reduce-scatter is not "
-              "built); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this path is one tensor-parallel rank's share on one GPU (the "
+              "cross-GPU reduce-scatter is not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -166,88 +268,54 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rpl.lib()
-    wid = {"prefill": 3, "long_prefill": 4, "tiny": 1}[args.workload]
-    wl = synth.WORKLOADS[wid]
-    w8 = synth.WORKLOADS[5] if wid == 3 else None
-    log(f"workload {wl.name}: m={wl.m} k_shard={wl.k_shard} n={wl.n} tp={wl.tp}"
-        f"{' + w8a8 twin' if w8 else ''}")
-    d = build_inputs(wl, w8, torch)
-    mc = wl.m_chunk
-    dev = torch.device("cuda")
-    p0 = torch.empty((wl.m_pad, wl.n), dtype=torch.bfloat16, device=dev)
-    q0 = torch.empty((w8.m_pad, w8.n), dtype=torch.bfloat16, device=dev) if w8 else None
-    y = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
-    ro = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
-    # the peers' chunk-0 partials: data this rank receives (produced once, before timing)
-    peer_chunks = [rpl.rpl_partial(px, pw, 1) for px, pw in zip(d["peer_x"], d["peer_w"])]
-    torch.cuda.synchronize()
+    wl = synth.WORKLOADS[WORKLOAD_IDS[args.workload]]
+    path = Path(wl, torch, rpl, args.copies)
+    small = wl.m_pad <= 16
+    runner = path.run_graphs if small else path.run
+    ms_per_step, kern, period = runner(args.steps, args.warmup)
+    kernels = path.kernels_report(kern, period)
+    pn = path.names[0]
+    if small:  # decode: bound by the weight stream
+        value, unit = (wl.partial_bytes() + wl.reduce_bytes()) / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        roofline = {"bound": "hbm", "kernel": pn, "achieved": kernels[pn]["GB/s"], "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": kernels[pn]["frac_hbm"], "traffic": load_traffic(pn, wl.name)}
+    else:
+        value, unit = wl.gemm_flops() / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        peak = PEAK_I8_TOPS if path.w8 else PEAK_BF16_TFLOPS
+        rate = kernels[pn]["TOP/s" if path.w8 else "TFLOP/s"]
+        roofline = {"bound": "mfma", "kernel": pn, "achieved": rate, "peak": peak,
+                    "unit": "TOP/s" if path.w8 else "TFLOP/s", "frac": rate / peak,
+                    "traffic": load_traffic(pn, wl.name)}
+    sets_used = len(path.sets)
+    del path
+    torch.cuda.empty_cache()
 
-    names = ["partial_bf16"] + (["partial_w8a8"] if w8 else []) + ["reduce_rmsnorm"]
-
-    def step(evs=None):
-        """One pass of the path; evs[k] = (start, end) HIP events around kernel k."""
-        def run(k, fn):
-            if evs is not None:
-                evs[k][0].record()
-            fn()
-            if evs is not None:
-                evs[k][1].record()
-        run(0, lambda: rpl.rpl_partial(d["x0"], d["w0"], wl.tp, out=p0))
-        if w8:
-            run(1, lambda: rpl.rpl_w8a8_partial(d["xq"], d["sx"], d["wq"], d["sw"], w8.tp, out=q0))
-        run(len(names) - 1, lambda: rpl.rpl_reduce_chunk_rmsnorm([p0[:mc]] + peer_chunks, d["res"], d["gam"],
-                                                                  wl.eps, y=y, residual_out=ro))
-
-    for _ in range(args.warmup):
-        step()
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    kern_us = {nm: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(args.steps)])) * 1e3
-               for j, nm in enumerate(names)}
-
-    flops_bf16 = wl.gemm_flops()
-    ops_i8 = w8.gemm_flops() if w8 else 0.0
-    value = (flops_bf16 + ops_i8) / (ms_per_step * 1e-3) / 1e12
-    kernels = {"partial_bf16": {"us": kern_us["partial_bf16"], "flop": flops_bf16,
-                                "TFLOP/s": flops_bf16 / (kern_us["partial_bf16"] * 1e-6) / 1e12}}
-    kernels["partial_bf16"]["frac_bf16_peak"] = kernels["partial_bf16"]["TFLOP/s"] / PEAK_BF16_TFLOPS
-    if w8:
-        tops = ops_i8 / (kern_us["partial_w8a8"] * 1e-6) / 1e12
-        kernels["partial_w8a8"] = {"us": kern_us["partial_w8a8"], "op": ops_i8, "TOP/s": tops,
-                                   "frac_int8_peak": tops / PEAK_I8_TOPS, "frac_bf16_peak": tops / PEAK_BF16_TFLOPS}
-    rb = wl.reduce_bytes()
-    kernels["reduce_rmsnorm"] = {"us": kern_us["reduce_rmsnorm"], "bytes": rb,
-                                 "GB/s": rb / (kern_us["reduce_rmsnorm"] * 1e-6) / 1e9}
-    kernels["reduce_rmsnorm"]["frac_hbm"] = kernels["reduce_rmsnorm"]["GB/s"] / PEAK_HBM_GBS
-
-    dom = kernels["partial_bf16"]
-    roofline = {"bound": "mfma", "kernel": "partial_bf16", "achieved": dom["TFLOP/s"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom["frac_bf16_peak"],
-                "traffic": load_traffic("partial_bf16", wl.name)}
-
-    extra = {}
-    if not args.no_decode:
-        extra["decode"] = time_decode(torch, rpl, steps=200, copies=40)
+    side = {}
+    if not args.no_side and args.workload == "prefill":
+        for key in ("w8a8", "decode", "long_prefill"):
+            swl = synth.WORKLOADS[WORKLOAD_IDS[key]]
+            sp = Path(swl, torch, rpl, args.copies)
+            if swl.m_pad <= 16:
+                s_ms, s_kern, s_period = sp.run_graphs(200, 3)
+            else:
+                s_ms, s_kern, s_period = sp.run(10, 3)
+            side[key] = {"workload": swl.name, "ms_per_step": s_ms, "input_sets_rotated": len(sp.sets),
+                         "kernels": sp.kernels_report(s_kern, s_period)}
+            del sp
+            torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, w8, args.cpu_budget)
+    if not args.no_cpu_baseline and wl.kind != "w8a8":
+        cpu = cpu_baseline(wl, args.cpu_budget)
 
     line = {
-        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16+i8" if w8 else "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + (" + w8a8 twin" if w8 else ""), "m_tokens": wl.m,
-                   "k_full": wl.k_full, "tp": wl.tp, "k_shard": wl.k_shard, "n": wl.n, "m_chunk": mc,
-                   "parallelism": f"one TP rank of {wl.tp} (peers emulated)"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "side": extra,
+        "vs_baseline": None, "dtype": "i8" if wl.kind == "w8a8" else "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "m_tokens": wl.m, "k_full": wl.k_full, "tp": wl.tp, "k_shard": wl.k_shard,
+                   "n": wl.n, "m_chunk": wl.m_chunk, "parallelism": f"one TP rank of {wl.tp} (peers emulated)",
+                   "input_sets_rotated": sets_used},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "side": side,
         "kernel_sources_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

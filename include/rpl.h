@@ -93,7 +93,8 @@ typedef enum {
  * RPL_ERR_NULL        w is NULL, or m > 0 and x or out is NULL
  * RPL_ERR_INVALID     m < 0, n < 1, k < 1, tp < 1, ldx < k, ldw < k, out overlaps x/w
  * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; k, n, ldx or ldw not a multiple of 8;
- *                     any pointer not 16-byte aligned; m, n or k >= 2^31
+ *                     any pointer not 16-byte aligned; m, n or k >= 2^31;
+ *                     a row stride of 8 MiB or more (ldx or ldw >= 2^22)
  * RPL_ERR_LAUNCH      the kernel launch failed (e.g. no gfx950 device)
  */
 rpl_status rpl_partial(const rpl_bf16 *x, int64_t ldx,
@@ -174,7 +175,8 @@ rpl_status rpl_reduce_chunk_rmsnorm(const rpl_bf16 *const *partials, int32_t tp,
  * RPL_ERR_INVALID     m < 0, n < 1, k < 1, tp < 1, ldx < k, ldw < k, overlaps
  * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; k, ldx or ldw not a multiple of 16;
  *                     n not a multiple of 8; xq, wq, out, acc not 16-byte
- *                     aligned or scales not 4-byte aligned; m, n or k >= 2^31
+ *                     aligned or scales not 4-byte aligned; m, n or k >= 2^31;
+ *                     a row stride of 8 MiB or more (ldx or ldw >= 2^23)
  * RPL_ERR_LAUNCH      the kernel launch failed
  */
 rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,

@@ -11,7 +11,8 @@
 // reduce-scatter send layout [tp][M_pad/tp][n]; pad rows are zero.
 //
 // Two kernels:
-//  * prefill: the LDS double-buffered MFMA tile engine of gemm_nt.h with
+//  * prefill: the MFMA tile engine of gemm_nt.h (operands DMA'd straight to
+//    LDS, double-buffered, fragment reads prefetched across the barrier) with
 //    v_mfma_f32_16x16x32_bf16 and fp32 accumulators;
 //  * decode (M_pad <= 16): the weight stream dominates (a few tokens against
 //    the whole weight), so each workgroup owns 16 output columns, its waves
@@ -38,18 +39,18 @@ struct Bf16Op {
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool CHECK>
+template <int BM, int BN, int WM, int WN, bool PRIO>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN)))
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 gemm_bf16_prefill_kernel(GemmShape g, uint16_t *out) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * KT_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (BM + BN) * KT_BYTES + PF_BYTES];
     Bf16Op op{out, g.n};
-    gemm_nt_tile<BM, BN, WM, WN, CHECK>(g, op, smem);
+    gemm_nt_tile<BM, BN, WM, WN, PRIO>(g, op, smem);
 }
 
 // ---------------------------------------------------------------- decode path
-constexpr int DEC_WAVES = 8;
-constexpr int DEC_BATCH = 8;  // K steps (32 values each) whose loads are issued together
+constexpr int DEC_WAVES = 4;
+constexpr int DEC_BATCH = 16;  // K steps (32 values each) whose loads are issued together
 
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * DEC_WAVES, 64 * DEC_WAVES)))
 gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w,
@@ -97,16 +98,10 @@ gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint1
 }
 
 // ---------------------------------------------------------------- launchers
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool PRIO>
 static hipError_t launch_prefill(const GemmShape &g, uint16_t *out, hipStream_t st) {
     const int nt = ((g.m_pad + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    const bool full = g.m == g.m_pad && g.m % BM == 0 && g.n % BN == 0 && g.kbytes % KT_BYTES == 0;
-    if (full)
-        hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, false>), dim3(nt), dim3(64 * WM * WN), 0, st,
-                           g, out);
-    else
-        hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, true>), dim3(nt), dim3(64 * WM * WN), 0, st,
-                           g, out);
+    hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, PRIO>), dim3(nt), dim3(64 * WM * WN), 0, st, g, out);
     return hipGetLastError();
 }
 
@@ -119,8 +114,8 @@ hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w
     }
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),
                 ldx * 2, ldw * 2, m, m_pad, n, k * 2, 4};
-    if (pick_tile_n(m_pad, n) == 224) return launch_prefill<256, 224, 4, 2>(g, out, st);
-    return launch_prefill<256, 256, 2, 4>(g, out, st);
+    if (pick_tile_n(m_pad, n) == 224) return launch_prefill<256, 224, 4, 2, false>(g, out, st);
+    return launch_prefill<256, 256, 2, 4, true>(g, out, st);
 }
 
 }  // namespace rpl

@@ -7,13 +7,32 @@
 // copy that the xLLM pull request #1890 "feat: add FlashComm1 and MMRS fusion
 // support for Qwen3.5 NPU" caches in its review thread; here it is not needed).
 //
-// One workgroup computes a BM x BN output tile with WM x WN wavefronts.  A K
-// step stages 128 bytes of every operand row (64 bf16 or 128 int8 values)
-// through LDS, double-buffered: the global loads of step t+1 are issued before
-// the MFMAs of step t and written to the other LDS buffer afterwards, so one
-// barrier per step suffices.  LDS rows are 128 bytes; the 16-byte chunk c of
-// tile row r lives at chunk (c ^ (r & 7)), which spreads the 16 rows that an
-// MFMA fragment read touches over distinct banks.
+// One workgroup computes a BM x BN output tile with WM x WN wavefronts.
+//
+// Staging.  A K step stages 128 bytes of every operand row (64 bf16 or 128
+// int8 values) in LDS, double-buffered.  Rows reach LDS straight from memory
+// with buffer_load_dwordx4 ... lds (no VGPR round trip): one wave instruction
+// fills 8 rows x 128 bytes.  The buffer descriptor of each operand starts at
+// the tile's first row and its record count ends at the operand's last valid
+// byte, so rows past m (or n) read as zero in hardware; K-tail chunks get an
+// out-of-range offset and read as zero too.  Ragged shapes therefore need no
+// separate bounds-checked kernel.  In LDS the 16-byte chunk c of tile row r
+// sits at chunk (c ^ (r & 7)), so the 16 rows one MFMA fragment read touches
+// fall on distinct banks (zero bank conflicts measured with rocprofv3).
+//
+// L2 prefetch.  Two buffers of LDS give the DMA of step k+1 only one step of
+// lead, less than the latency of HBM under load.  So each step also touches
+// the lines of step k+PF_DIST once -- one 4-byte DMA per 128-byte line into a
+// 256-byte LDS scratch slot that is never read -- so that the real DMA finds
+// them in L2.  The barrier waits for every load but that newest one.
+//
+// Schedule.  Per K step each wave reads its fragments for the two 32-deep
+// halves of the step from LDS and issues its MFMAs.  The second half's
+// fragments are read before the barrier that publishes the next buffer, and
+// the second half's MFMAs run after it, while the first-half fragments of the
+// next step are being read: the barrier and the LDS read latency hide behind
+// MFMA work.  The barrier waits only for this wave's DMA of the next buffer
+// and for its own reads of the current one.
 //
 // MFMA operand roles are swapped (A <- weight rows, B <- activation rows) so
 // that each lane's 4 accumulators are 4 consecutive output columns of one
@@ -31,17 +50,25 @@ namespace rpl {
 
 constexpr int KT_BYTES = 128;  // bytes of K staged per step, per operand row
 constexpr int NUM_XCD = 8;
+constexpr int PF_DIST = 2;     // L2 prefetch distance, in K steps
+constexpr int PF_BYTES = 256;  // LDS sink of the prefetch loads (64 lanes x 4 bytes)
+// Largest operand row stride (bytes) the 32-bit buffer offsets of a 256-row tile can address.
+constexpr int64_t MAX_LD_BYTES = int64_t(1) << 23;
 
 struct GemmShape {
     const uint8_t *x;    // activation shard, byte pointer, row stride ldx bytes
     const uint8_t *w;    // weight shard, byte pointer, row stride ldw bytes
-    int64_t ldx, ldw;    // bytes
+    int64_t ldx, ldw;    // bytes (< MAX_LD_BYTES)
     int m;               // valid activation rows
     int m_pad;           // output rows (rows m..m_pad-1 are the zero padding)
     int n;               // output columns
     int kbytes;          // K in bytes (multiple of 16)
     int group_m;         // tile-row band height of the XCD-aware order
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int32_t RSRC_DWORD3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t OOB_OFFSET = 0x80000000u; // beyond every record count: reads as zero
 
 // Map the hardware block id to an output tile (tm, tn).
 __device__ __forceinline__ void tile_of_block(int bid, int nt_m, int nt_n, int group_m, int &tm, int &tn) {
@@ -59,22 +86,34 @@ __device__ __forceinline__ void tile_of_block(int bid, int nt_m, int nt_n, int g
 
 __device__ __forceinline__ int swz_off(int row, int chunk) { return row * KT_BYTES + ((chunk ^ (row & 7)) << 4); }
 
+// Buffer descriptor over rows [r0, rows) of a row-major operand with row stride ld bytes
+// and kbytes valid bytes per row; rows at or past `rows` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int r0, int rows, int64_t ld,
+                                                            int kbytes) {
+    const bool live = r0 < rows;
+    const int64_t start = (int64_t)r0 * ld;
+    const int64_t span = (int64_t)(rows - 1) * ld + kbytes;  // bytes from row 0 to the last valid byte
+    const uint32_t nrec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)min<int64_t>(span - start, 0x7FFFFFFF) : 0u);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base + (live ? start : 0)), (short)0, (int)nrec,
+                                             RSRC_DWORD3);
+}
+
 // Op supplies: Frag (16-byte operand), Acc (4-lane accumulator), mfma(), zero(),
-// and the epilogue store(acc, m_row, n_col, valid_m) for 4 consecutive columns.
-template <int BM, int BN, int WM, int WN, bool CHECK, class Op>
+// and the epilogue store(acc, m_row, n_col) of 4 consecutive columns.
+// smem: 2 * (BM + BN) * KT_BYTES + PF_BYTES bytes of LDS.
+template <int BM, int BN, int WM, int WN, bool PRIO, class Op>
 __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, uint8_t *smem) {
-    constexpr int T = 64 * WM * WN;
+    constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
-    constexpr int A_CH = BM * 8, B_CH = BN * 8;  // 16-byte chunks per K step
-    constexpr int A_PER = (A_CH + T - 1) / T, B_PER = (B_CH + T - 1) / T;
-    constexpr int STAGE = (BM + BN) * KT_BYTES;
+    constexpr int GA = BM / 8, GB = BN / 8;  // 8-row (1 KB) groups per operand per step
+    static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
+    static_assert(BM % 64 == 0 && (BM + BN + 63) / 64 == NW, "one prefetch instruction per wave and operand");
     using Frag = typename Op::Frag;
     using Acc = typename Op::Acc;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS DMA bases go in M0
     const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
 
     int tm, tn;
@@ -83,42 +122,48 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
     const int m0 = tm * BM, n0 = tn * BN;
     const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
 
-    u32x4 ra[A_PER], rb[B_PER];
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
+    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
 
-    auto gload = [&](int kt) {
-        const int kb = kt * KT_BYTES;
+    // DMA lane mapping: lane writes LDS chunk (lane & 7) of row (lane >> 3) of its
+    // 8-row group, so it fetches logical chunk (lane & 7) ^ row.
+    const int lr = lane >> 3;
+    const int pc = (lane & 7) ^ lr;
+    auto issue = [&](int kt, uint8_t *buf) {
+        const int kb = kt * KT_BYTES + pc * 16;
+        const bool kin = kb < g.kbytes;
 #pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            const int i = tid + j * T;
-            if (A_CH % T == 0 || i < A_CH) {
-                const int row = i >> 3, c = i & 7;
-                const int grow = m0 + row, kbyte = kb + c * 16;
-                const bool ok = !CHECK || (grow < g.m && kbyte < g.kbytes);
-                ra[j] = ok ? ld16(g.x + (int64_t)grow * g.ldx + kbyte) : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < (GA + NW - 1) / NW; ++j) {
+            const int gi = wave + j * NW;
+            if (GA % NW == 0 || gi < GA) {
+                const uint32_t v = kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
             }
         }
 #pragma unroll
-        for (int j = 0; j < B_PER; ++j) {
-            const int i = tid + j * T;
-            if (B_CH % T == 0 || i < B_CH) {
-                const int row = i >> 3, c = i & 7;
-                const int grow = n0 + row, kbyte = kb + c * 16;
-                const bool ok = !CHECK || (grow < g.n && kbyte < g.kbytes);
-                rb[j] = ok ? ld16(g.w + (int64_t)grow * g.ldw + kbyte) : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < (GB + NW - 1) / NW; ++j) {
+            const int gj = wave + j * NW;
+            if (GB % NW == 0 || gj < GB) {
+                const uint32_t v = kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
+                                                         0, 0, 0);
             }
         }
     };
-    auto sstore = [&](int buf) {
-        uint8_t *base = smem + buf * STAGE;
-#pragma unroll
-        for (int j = 0; j < A_PER; ++j) {
-            const int i = tid + j * T;
-            if (A_CH % T == 0 || i < A_CH) st16(base + swz_off(i >> 3, i & 7), ra[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < B_PER; ++j) {
-            const int i = tid + j * T;
-            if (B_CH % T == 0 || i < B_CH) st16(base + BM * KT_BYTES + swz_off(i >> 3, i & 7), rb[j]);
+
+    // L2 prefetch of step kt: wave w touches tile rows [64w, 64w + 64) (activation rows
+    // first, then weight rows), one lane per row.
+    uint8_t *s0 = smem, *s1 = smem + (BM + BN) * KT_BYTES, *sink = smem + 2 * (BM + BN) * KT_BYTES;
+    auto prefetch = [&](int kt) {
+        const int r = wave * 64 + lane;
+        const int kb = kt * KT_BYTES;
+        if (wave * 64 < BM) {
+            const uint32_t v = (kb < g.kbytes) ? (uint32_t)(r * g.ldx + kb) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
+        } else {
+            const int rr = r - BM;
+            const uint32_t v = (rr < BN && kb < g.kbytes) ? (uint32_t)(rr * g.ldw + kb) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)sink, 4, v, 0, 0, 0);
         }
     };
 
@@ -128,35 +173,61 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
 #pragma unroll
         for (int b = 0; b < FN; ++b) acc[a][b] = Op::zero();
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
     const int frow = lane & 15, fchunk = lane >> 4;
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < ksteps) gload(kt + 1);
-        const uint8_t *sa = smem + cur * STAGE;
+    auto load_frags = [&](const uint8_t *sa, int half, Frag *xf, Frag *wf) {
         const uint8_t *sb = sa + BM * KT_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            Frag xf[FM], wf[FN];
+        for (int a = 0; a < FM; ++a)
+            xf[a] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
+                                                 sa + swz_off(wm0 + a * 16 + frow, half * 4 + fchunk)));
 #pragma unroll
-            for (int a = 0; a < FM; ++a)
-                xf[a] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
-                                                     sa + swz_off(wm0 + a * 16 + frow, kk * 4 + fchunk)));
+        for (int b = 0; b < FN; ++b)
+            wf[b] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
+                                                 sb + swz_off(wn0 + b * 16 + frow, half * 4 + fchunk)));
+    };
+    auto mfmas = [&](const Frag *xf, const Frag *wf) {
 #pragma unroll
-            for (int b = 0; b < FN; ++b)
-                wf[b] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
-                                                     sb + swz_off(wn0 + b * 16 + frow, kk * 4 + fchunk)));
+        for (int a = 0; a < FM; ++a)
 #pragma unroll
-            for (int a = 0; a < FM; ++a)
+            for (int b = 0; b < FN; ++b) acc[a][b] = Op::mfma(wf[b], xf[a], acc[a][b]);
+    };
+    // Workgroup barrier once this wave's reads of the current buffer (the fragments
+    // passed in: the empty asm statements make the compiler wait for them) have
+    // returned and its DMA into the next buffer has landed (vmcnt(1): all loads but
+    // the prefetch issued after that DMA).  sched_barrier keeps the compiler from
+    // moving work across it.
+    auto barrier = [&](const Frag *xf, const Frag *wf) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int b = 0; b < FN; ++b) acc[a][b] = Op::mfma(wf[b], xf[a], acc[a][b]);
-        }
-        if (kt + 1 < ksteps) sstore(cur ^ 1);
-        __syncthreads();
+        for (int a = 0; a < FM; ++a) asm volatile("" ::"v"(xf[a]));
+#pragma unroll
+        for (int b = 0; b < FN; ++b) asm volatile("" ::"v"(wf[b]));
+        asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    Frag xa[FM], wa[FN], xb[FM], wb[FN];
+    for (int d = 1; d < PF_DIST; ++d) prefetch(d);
+    issue(0, s0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (PRIO) __builtin_amdgcn_s_setprio(1);
+    load_frags(s0, 0, xa, wa);
+    uint8_t *cur = s0, *nxt = s1;
+    for (int kt = 0; kt < ksteps; ++kt) {
+        const bool more = kt + 1 < ksteps;
+        if (more) issue(kt + 1, nxt);
+        prefetch(kt + PF_DIST);  // past the end: out of range, reads nothing
+        load_frags(cur, 1, xb, wb);
+        mfmas(xa, wa);
+        barrier(xb, wb);
+        if (more) load_frags(nxt, 0, xa, wa);
+        mfmas(xb, wb);
+        uint8_t *t = cur;
+        cur = nxt;
+        nxt = t;
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
+    if (PRIO) __builtin_amdgcn_s_setprio(0);
 
     // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
 #pragma unroll
@@ -165,7 +236,7 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
 #pragma unroll
         for (int b = 0; b < FN; ++b) {
             const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
-            if (!CHECK || (mrow < g.m_pad && ncol < g.n)) op.store(acc[a][b], mrow, ncol);
+            if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
         }
     }
 }

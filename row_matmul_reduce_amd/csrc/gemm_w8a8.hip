@@ -6,9 +6,9 @@
 // token, int8 weight codes with a required fp32 scale per output channel; the
 // integer product is accumulated exactly and dequantised to the bf16 partial.
 //
-// Same LDS double-buffered tile engine as the bf16 partial (gemm_nt.h): a K
-// step stages 128 int8 values per row, consumed by two
-// v_mfma_i32_16x16x64_i8 per fragment pair with exact int32 accumulators.
+// Same tile engine as the bf16 partial (gemm_nt.h): a K step stages 128 int8
+// values per row, consumed by two v_mfma_i32_16x16x64_i8 per fragment pair
+// with exact int32 accumulators.
 // Epilogue, in this order and with no fused multiply-add:
 //   out = bf16_rne( (float(acc) * x_scale[m]) * w_scale[n] )
 // and, when requested, the int32 accumulators themselves.
@@ -43,22 +43,18 @@ struct W8a8Op {
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool CHECK>
+template <int BM, int BN, int WM, int WN, bool PRIO>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN)))
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 gemm_w8a8_kernel(GemmShape g, W8a8Op op) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * KT_BYTES];
-    gemm_nt_tile<BM, BN, WM, WN, CHECK>(g, op, smem);
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (BM + BN) * KT_BYTES + PF_BYTES];
+    gemm_nt_tile<BM, BN, WM, WN, PRIO>(g, op, smem);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool PRIO>
 static hipError_t launch_w8a8(const GemmShape &g, const W8a8Op &op, hipStream_t st) {
     const int nt = ((g.m_pad + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    const bool full = g.m == g.m_pad && g.m % BM == 0 && g.n % BN == 0 && g.kbytes % KT_BYTES == 0;
-    if (full)
-        hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, false>), dim3(nt), dim3(64 * WM * WN), 0, st, g, op);
-    else
-        hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, true>), dim3(nt), dim3(64 * WM * WN), 0, st, g, op);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, PRIO>), dim3(nt), dim3(64 * WM * WN), 0, st, g, op);
     return hipGetLastError();
 }
 
@@ -68,8 +64,8 @@ hipError_t launch_partial_w8a8(const int8_t *xq, int64_t ldx, const float *sx, c
     GemmShape g{reinterpret_cast<const uint8_t *>(xq), reinterpret_cast<const uint8_t *>(wq), ldx, ldw, m, m_pad, n,
                 k, 4};
     W8a8Op op{out, acc, sx, sw, m, n};
-    if (pick_tile_n(m_pad, n) == 224) return launch_w8a8<256, 224, 4, 2>(g, op, st);
-    return launch_w8a8<256, 256, 2, 4>(g, op, st);
+    if (pick_tile_n(m_pad, n) == 224) return launch_w8a8<256, 224, 4, 2, false>(g, op, st);
+    return launch_w8a8<256, 256, 2, 4, true>(g, op, st);
 }
 
 }  // namespace rpl

@@ -17,9 +17,11 @@
 // RW wavefronts; lane t of the team holds 16-byte chunks t, t + 64*RW, ... of
 // the row (CPL of them) in fp32 registers, so the row is read once, the sum of
 // squares is a wavefront butterfly (plus an LDS exchange between the team's
-// waves when RW > 1), and both outputs are written from registers.  The
-// residual is read before either output is written, so residual_out may be
-// the residual buffer itself.
+// waves when RW > 1), and both outputs are written from registers.  All loads
+// of a group of G partials (and the residual and gamma up front) are issued
+// before any of them is consumed, so a row costs one or a few memory round
+// trips instead of one per chunk.  The residual is read before either output
+// is written, so residual_out may be the residual buffer itself.
 #include "rpl_device.h"
 #include "rpl_launch.h"
 
@@ -35,39 +37,55 @@ template <int CPL, int RW>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
 reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t *__restrict__ residual,
                       const uint16_t *__restrict__ gamma, float eps, uint16_t *y, uint16_t *residual_out) {
-    constexpr int ROWS = 4 / RW;  // rows per 256-thread workgroup
+    constexpr int ROWS = 4 / RW;            // rows per 256-thread workgroup
+    constexpr int G = CPL <= 4 ? 4 : 2;     // partials whose loads are in flight together
     __shared__ float team_sum[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * ROWS + wave / RW;
     const int t = (wave % RW) * 64 + lane;
     const int nch = n >> 3;
-    const bool row_ok = row < m_chunk;  // RW > 1: the whole workgroup shares one row
+    const bool row_ok = row < m_chunk;      // RW > 1: the whole workgroup shares one row
+    const int64_t rbase = (int64_t)row * n;
 
     float h[CPL][8];
-    const int64_t rbase = (int64_t)row * n;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+    u32x4 rv[CPL], gv[CPL];
     if (row_ok) {
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = t + j * 64 * RW;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
-            if (c < nch) {
-                for (int s = 0; s < tp; ++s) {
-                    const u32x4 v = ld16(P.p[s] + rbase + c * 8);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        h[j][2 * q] += bf16_lo(v[q]);
-                        h[j][2 * q + 1] += bf16_hi(v[q]);
-                    }
-                }
-                const u32x4 r = ld16(residual + rbase + c * 8);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    h[j][2 * q] += bf16_lo(r[q]);
-                    h[j][2 * q + 1] += bf16_hi(r[q]);
-                }
-            }
+            rv[j] = c < nch ? ld16(residual + rbase + c * 8) : u32x4{0, 0, 0, 0};
+            gv[j] = c < nch ? ld16(gamma + c * 8) : u32x4{0, 0, 0, 0};
         }
+        for (int s0 = 0; s0 < tp; s0 += G) {
+            u32x4 v[G][CPL];
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const int c = t + j * 64 * RW;
+                    v[q][j] = (s0 + q < tp && c < nch) ? ld16(P.p[s0 + q] + rbase + c * 8) : u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+#pragma unroll
+                for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        h[j][2 * e] += bf16_lo(v[q][j][e]);
+                        h[j][2 * e + 1] += bf16_hi(v[q][j][e]);
+                    }
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h[j][2 * e] += bf16_lo(rv[j][e]);
+                h[j][2 * e + 1] += bf16_hi(rv[j][e]);
+            }
     }
     float ss = 0.f;
 #pragma unroll
@@ -79,8 +97,9 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
         if (lane == 0) team_sum[wave] = ss;
         __syncthreads();
         ss = 0.f;
+        const int tb = (wave / RW) * RW;  // first wave of this row's team
 #pragma unroll
-        for (int v = 0; v < RW; ++v) ss += team_sum[v];
+        for (int v = 0; v < RW; ++v) ss += team_sum[tb + v];
     }
     if (!row_ok) return;
     const float inv = rsqrtf(ss / (float)n + eps);
@@ -88,13 +107,12 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
     for (int j = 0; j < CPL; ++j) {
         const int c = t + j * 64 * RW;
         if (c < nch) {
-            const u32x4 gv = ld16(gamma + c * 8);
             u32x4 yo, ro;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float a = h[j][2 * q], b = h[j][2 * q + 1];
                 ro[q] = pack_bf16x2(a, b);
-                yo[q] = pack_bf16x2(bf16_lo(gv[q]) * (a * inv), bf16_hi(gv[q]) * (b * inv));
+                yo[q] = pack_bf16x2(bf16_lo(gv[j][q]) * (a * inv), bf16_hi(gv[j][q]) * (b * inv));
             }
             st16(residual_out + rbase + c * 8, ro);
             st16(y + rbase + c * 8, yo);
@@ -113,20 +131,24 @@ static hipError_t launch_rr(const PartialPtrs &p, int tp, int m_chunk, int n, co
 
 hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
                                  const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
+    // The fewest wavefronts per row that keep each lane at <= 4 chunks (32 values),
+    // or 4 wavefronts with up to 8 chunks for the widest rows (n <= 16384).
     const int nch = n / 8;
-    if (nch <= 64 * 12) {  // one wavefront per row, up to 12 chunks (96 values) per lane
+    if (nch <= 64 * 4) {
         switch ((nch + 63) / 64) {
-#define RR1(C) \
-    case C: return launch_rr<C, 1>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
-            RR1(1) RR1(2) RR1(3) RR1(4) RR1(5) RR1(6) RR1(7) RR1(8) RR1(9) RR1(10) RR1(11) RR1(12)
-#undef RR1
+#define RR(C, W) \
+    case C: return launch_rr<C, W>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
+            RR(1, 1) RR(2, 1) RR(3, 1) RR(4, 1)
         }
-    }
-    switch ((nch + 255) / 256) {  // four wavefronts per row (n <= 16384)
-#define RR4(C) \
-    case C: return launch_rr<C, 4>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
-        RR4(1) RR4(2) RR4(3) RR4(4) RR4(5) RR4(6) RR4(7) RR4(8)
-#undef RR4
+    } else if (nch <= 128 * 4) {
+        switch ((nch + 127) / 128) {
+            RR(3, 2) RR(4, 2)
+        }
+    } else {
+        switch ((nch + 255) / 256) {
+            RR(3, 4) RR(4, 4) RR(5, 4) RR(6, 4) RR(7, 4) RR(8, 4)
+#undef RR
+        }
     }
     return hipErrorInvalidValue;
 }

@@ -19,6 +19,9 @@
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Operand row strides (bytes) must stay below 8 MiB: the tile engine addresses a
+// 256-row tile with 32-bit buffer offsets.
+constexpr int64_t kMaxLdBytes = int64_t(1) << 23;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -60,6 +63,7 @@ rpl_status rpl_partial(const rpl_bf16 *x, int64_t ldx, const rpl_bf16 *w, int64_
     if (tp > RPL_MAX_TP || k % 8 || n % 8 || ldx % 8 || ldw % 8) return RPL_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16)) return RPL_ERR_UNSUPPORTED;
     if (m_pad > kMaxDim || n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (ldx * 2 >= kMaxLdBytes || ldw * 2 >= kMaxLdBytes) return RPL_ERR_UNSUPPORTED;
     if (m == 0) return RPL_OK;
     return launch_status(rpl::launch_partial_bf16(x, ldx, w, ldw, out, (int)m, (int)m_pad, (int)n, (int)k,
                                                   static_cast<hipStream_t>(stream)));
@@ -121,6 +125,7 @@ rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
         !aligned(x_scale, 4) || !aligned(w_scale, 4))
         return RPL_ERR_UNSUPPORTED;
     if (m_pad > kMaxDim || n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (ldx >= kMaxLdBytes || ldw >= kMaxLdBytes) return RPL_ERR_UNSUPPORTED;
     if (m == 0) return RPL_OK;
     return launch_status(rpl::launch_partial_w8a8(xq, ldx, x_scale, wq, ldw, w_scale, out, acc, (int)m, (int)m_pad,
                                                   (int)n, (int)k, static_cast<hipStream_t>(stream)));

@@ -159,7 +159,7 @@ def gamma(wl: Workload) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ w8a8 path
-def w8a8_inputs(wl: Workload, rows: int | None = None):
+def w8a8_inputs(wl: Workload, rows: int | None = None, shard: int = 0):
     """int8 activations with a per-token fp32 scale, int8 weights with a
     per-channel fp32 scale.
 
@@ -167,15 +167,15 @@ def w8a8_inputs(wl: Workload, rows: int | None = None):
     N(0,1) data: scale = row absmax / 127 (fp32), code = round-half-even of
     x / scale clamped to [-127, 127].  This is how the int8 tensor and its scale
     are made, not a step of the path (the path consumes codes and scales).
-    Returns (xq [r, k] int8, sx [r] fp32, wq [n, k] int8, sw [n] fp32).
+    Returns (xq [r, k] int8, sx [r] fp32, wq [n, k] int8, sw [n] fp32) of rank `shard`.
     """
     r = wl.m if rows is None else min(rows, wl.m)
-    xf = _rng(wl, T_XFP, 0).standard_normal((r, wl.k_shard), dtype=np.float32)
+    xf = _rng(wl, T_XFP, shard).standard_normal((r, wl.k_shard), dtype=np.float32)
     absmax = np.max(np.abs(xf), axis=1)
     sx = (absmax / np.float32(127.0)).astype(np.float32)
     sx = np.where(sx > 0, sx, np.float32(1.0)).astype(np.float32)
     q = np.rint(xf / sx[:, None])
     xq = np.clip(q, -127, 127).astype(np.int8)
-    wq = _rng(wl, T_W, 0).integers(-127, 128, (wl.n, wl.k_shard), dtype=np.int8)
-    sw = _rng(wl, T_WSCALE, 0).uniform(1e-3, 1e-2, wl.n).astype(np.float32)
+    wq = _rng(wl, T_W, shard).integers(-127, 128, (wl.n, wl.k_shard), dtype=np.int8)
+    sw = _rng(wl, T_WSCALE, shard).uniform(1e-3, 1e-2, wl.n).astype(np.float32)
     return np.ascontiguousarray(xq), sx, np.ascontiguousarray(wq), sw

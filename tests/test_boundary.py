@@ -93,6 +93,8 @@ def test_partial_validation():
         ((x + 2, k, w, k, o, m, n, k, tp), UNSUP),                # misaligned x
         ((x, k, w + 8, k, o, m, n, k, tp), UNSUP),                # misaligned w
         ((x, k, w, k, o + 4, m, n, k, tp), UNSUP),                # misaligned out
+        # row stride of 8 MiB or more (far-apart fake addresses: never dereferenced)
+        ((1 << 44, 1 << 22, 1 << 45, k, 1 << 46, m, n, k, tp), UNSUP),
         # too many rows (far-apart fake addresses: never dereferenced, no overlap)
         ((1 << 44, k, 1 << 45, k, 1 << 46, 1 << 31, n, k, tp), UNSUP),
     ]
