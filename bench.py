@@ -253,6 +253,8 @@ def main():
     ap.add_argument("--no-side", action="store_true", help="skip the side paths (w8a8, decode, long prefill)")
     ap.add_argument("--copies", type=int, default=0,
                     help="input sets cycled through (0: enough to exceed twice the 256 MB MALL)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy three times (scales HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -268,6 +270,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     rpl.lib()
+    if args.copy_calibration:
+        nbytes = 512 << 20
+        srcs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(i) for i in range(3)]
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        for src in srcs:
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}}))
+        return
     wl = synth.WORKLOADS[WORKLOAD_IDS[args.workload]]
     path = Path(wl, torch, rpl, args.copies)
     small = wl.m_pad <= 16
