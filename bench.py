@@ -213,6 +213,28 @@ class Path:
         return rep
 
 
+def library_reference(path, torch, steps: int):
+    """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
+    HBM-resident input sets, same stream and timing method, to show what the chip gives under the
+    bench's sustained load.  Its result is not used anywhere."""
+    wl = path.wl
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(3):
+        d = path.sets[i % len(path.sets)]
+        torch.matmul(d["x"], d["w"].t())
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        d = path.sets[i % len(path.sets)]
+        a.record()
+        torch.matmul(d["x"], d["w"].t())
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    rate = wl.gemm_flops() / (us * 1e-6) / 1e12
+    return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation",
+            "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS}
+
+
 def cpu_baseline(wl, budget_s: float):
     """The CPU oracle on the first R token rows of the same step (R sized to the time budget)."""
     import oracle
@@ -298,6 +320,9 @@ def main():
                     "unit": "TOP/s" if path.w8 else "TFLOP/s", "frac": rate / peak,
                     "traffic": load_traffic(pn, wl.name)}
     sets_used = len(path.sets)
+    reference = None
+    if not path.w8 and not small and not args.no_side:
+        reference = library_reference(path, torch, args.steps)
     del path
     torch.cuda.empty_cache()
 
@@ -327,6 +352,7 @@ def main():
                    "n": wl.n, "m_chunk": wl.m_chunk, "parallelism": f"one TP rank of {wl.tp} (peers emulated)",
                    "input_sets_rotated": sets_used},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "side": side,
+        "library_reference": reference,
         "kernel_sources_sha256_16": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -22,8 +22,8 @@
 //
 // L2 prefetch.  Two buffers of LDS give the DMA of step k+1 only one step of
 // lead, less than the latency of HBM under load.  So each step also touches
-// the lines of step k+PF_DIST once -- one 4-byte DMA per 128-byte line into a
-// 256-byte LDS scratch slot that is never read -- so that the real DMA finds
+// the lines of step k+PF (PF = 2 or 3) once -- one 4-byte DMA per 128-byte line
+// into a 256-byte LDS sink that is never read -- so that the real DMA finds
 // them in L2.  The barrier waits for every load but that newest one.
 //
 // Schedule.  Per K step each wave reads its fragments for the two 32-deep
@@ -41,7 +41,8 @@
 // Tile order is XCD-aware: the hardware deals workgroups round-robin to the 8
 // XCDs, so consecutive tile ids are remapped onto one XCD, and tiles are
 // walked in bands of GROUP_M tile rows so that the tiles an XCD runs at the
-// same time share activation rows and weight rows in that XCD's L2.
+// same time share activation rows and weight rows in that XCD's L2.  At most
+// 256 workgroups run (one per CU); each loops over its tiles.
 #pragma once
 
 #include "rpl_device.h"
@@ -50,7 +51,6 @@ namespace rpl {
 
 constexpr int KT_BYTES = 128;  // bytes of K staged per step, per operand row
 constexpr int NUM_XCD = 8;
-constexpr int PF_DIST = 2;     // L2 prefetch distance, in K steps
 constexpr int PF_BYTES = 256;  // LDS sink of the prefetch loads (64 lanes x 4 bytes)
 // Largest operand row stride (bytes) the 32-bit buffer offsets of a 256-row tile can address.
 constexpr int64_t MAX_LD_BYTES = int64_t(1) << 23;
@@ -100,9 +100,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
 
 // Op supplies: Frag (16-byte operand), Acc (4-lane accumulator), mfma(), zero(),
 // and the epilogue store(acc, m_row, n_col) of 4 consecutive columns.
+// Persistent tile loop: the grid has min(tiles, NUM_CU) workgroups and workgroup b
+// runs tiles b, b + grid, b + 2*grid, ... (grid is a multiple of 8 whenever it loops,
+// so a workgroup stays on one XCD's tile range).  A tile's first DMA is issued before
+// the previous tile's results are stored, so the stores overlap that load.
 // smem: 2 * (BM + BN) * KT_BYTES + PF_BYTES bytes of LDS.
-template <int BM, int BN, int WM, int WN, bool PRIO, class Op>
-__device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, uint8_t *smem) {
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, class Op>
+__device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op &op, uint8_t *smem) {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 16, FN = TN / 16;
@@ -115,20 +119,18 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS DMA bases go in M0
     const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
-
-    int tm, tn;
     const int nt_m = (g.m_pad + BM - 1) / BM, nt_n = (g.n + BN - 1) / BN;
-    tile_of_block(blockIdx.x, nt_m, nt_n, g.group_m, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int total = nt_m * nt_n;
     const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
-
-    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
+    uint8_t *s0 = smem, *s1 = smem + (BM + BN) * KT_BYTES, *sink = smem + 2 * (BM + BN) * KT_BYTES;
 
     // DMA lane mapping: lane writes LDS chunk (lane & 7) of row (lane >> 3) of its
     // 8-row group, so it fetches logical chunk (lane & 7) ^ row.
     const int lr = lane >> 3;
     const int pc = (lane & 7) ^ lr;
+    const int frow = lane & 15, fchunk = lane >> 4;
+
+    __amdgpu_buffer_rsrc_t rx, rw;
     auto issue = [&](int kt, uint8_t *buf) {
         const int kb = kt * KT_BYTES + pc * 16;
         const bool kin = kb < g.kbytes;
@@ -150,10 +152,8 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
             }
         }
     };
-
     // L2 prefetch of step kt: wave w touches tile rows [64w, 64w + 64) (activation rows
     // first, then weight rows), one lane per row.
-    uint8_t *s0 = smem, *s1 = smem + (BM + BN) * KT_BYTES, *sink = smem + 2 * (BM + BN) * KT_BYTES;
     auto prefetch = [&](int kt) {
         const int r = wave * 64 + lane;
         const int kb = kt * KT_BYTES;
@@ -168,12 +168,6 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
     };
 
     Acc acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = Op::zero();
-
-    const int frow = lane & 15, fchunk = lane >> 4;
     auto load_frags = [&](const uint8_t *sa, int half, Frag *xf, Frag *wf) {
         const uint8_t *sb = sa + BM * KT_BYTES;
 #pragma unroll
@@ -191,54 +185,84 @@ __device__ __forceinline__ void gemm_nt_tile(const GemmShape &g, const Op &op, u
 #pragma unroll
             for (int b = 0; b < FN; ++b) acc[a][b] = Op::mfma(wf[b], xf[a], acc[a][b]);
     };
-    // Workgroup barrier once this wave's reads of the current buffer (the fragments
-    // passed in: the empty asm statements make the compiler wait for them) have
-    // returned and its DMA into the next buffer has landed (vmcnt(1): all loads but
-    // the prefetch issued after that DMA).  sched_barrier keeps the compiler from
-    // moving work across it.
-    auto barrier = [&](const Frag *xf, const Frag *wf) {
-        __builtin_amdgcn_sched_barrier(0);
+    // Empty asm statements that take the fragments make the compiler wait for their LDS
+    // reads at that point (cheap where used: the reads have long returned) and keep its
+    // wait bookkeeping exact, so no later MFMA waits on reads it does not need.
+    auto landed = [&](const Frag *xf, const Frag *wf) {
 #pragma unroll
         for (int a = 0; a < FM; ++a) asm volatile("" ::"v"(xf[a]));
 #pragma unroll
         for (int b = 0; b < FN; ++b) asm volatile("" ::"v"(wf[b]));
-        asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+    };
+    // Workgroup barrier once this wave's reads of the current buffer have returned and
+    // its DMA into the next buffer has landed (vmcnt(PF ? 1 : 0): every load but the
+    // prefetch issued after that DMA).  sched_barrier keeps the compiler from moving
+    // work across it.
+    auto barrier = [&](const Frag *xf, const Frag *wf) {
         __builtin_amdgcn_sched_barrier(0);
+        landed(xf, wf);
+        if (PF > 0) asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
+    auto store_tile = [&](int m0, int n0) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            const int mrow = m0 + wm0 + a * 16 + frow;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
+                if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
+            }
+        }
     };
 
     Frag xa[FM], wa[FN], xb[FM], wb[FN];
-    for (int d = 1; d < PF_DIST; ++d) prefetch(d);
-    issue(0, s0);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (PRIO) __builtin_amdgcn_s_setprio(1);
-    load_frags(s0, 0, xa, wa);
-    uint8_t *cur = s0, *nxt = s1;
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const bool more = kt + 1 < ksteps;
-        if (more) issue(kt + 1, nxt);
-        prefetch(kt + PF_DIST);  // past the end: out of range, reads nothing
-        load_frags(cur, 1, xb, wb);
-        mfmas(xa, wa);
-        barrier(xb, wb);
-        if (more) load_frags(nxt, 0, xa, wa);
-        mfmas(xb, wb);
-        uint8_t *t = cur;
-        cur = nxt;
-        nxt = t;
+    int pm0 = 0, pn0 = 0;
+    bool have_prev = false;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        int tm, tn;
+        tile_of_block(t, nt_m, nt_n, g.group_m, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
+        rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
+        for (int d = 1; d < PF; ++d) prefetch(d);
+        issue(0, s0);  // every wave passed the previous tile's last barrier: no LDS reads remain
+        if (have_prev) store_tile(pm0, pn0);
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) acc[a][b] = Op::zero();
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (PRIO) __builtin_amdgcn_s_setprio(1);
+        load_frags(s0, 0, xa, wa);
+        landed(xa, wa);
+        uint8_t *cur = s0, *nxt = s1;
+        for (int kt = 0; kt < ksteps; ++kt) {
+            const bool more = kt + 1 < ksteps;
+            if (more) issue(kt + 1, nxt);
+            if (PF > 0) prefetch(kt + PF);  // past the end: out of range, reads nothing
+            load_frags(cur, 1, xb, wb);
+            mfmas(xa, wa);
+            barrier(xb, wb);
+            if (more) load_frags(nxt, 0, xa, wa);
+            mfmas(xb, wb);
+            landed(xa, wa);
+            uint8_t *tmp = cur;
+            cur = nxt;
+            nxt = tmp;
+        }
+        if (PRIO) __builtin_amdgcn_s_setprio(0);
+        pm0 = m0;
+        pn0 = n0;
+        have_prev = true;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
-    if (PRIO) __builtin_amdgcn_s_setprio(0);
-
-    // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
-#pragma unroll
-    for (int a = 0; a < FM; ++a) {
-        const int mrow = m0 + wm0 + a * 16 + frow;
-#pragma unroll
-        for (int b = 0; b < FN; ++b) {
-            const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
-            if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
-        }
-    }
+    if (have_prev) store_tile(pm0, pn0);
 }
+
+// Grid of the persistent tile loop.
+__host__ __device__ inline int persistent_grid(int tiles) { return tiles < 256 ? tiles : 256; }
 
 }  // namespace rpl

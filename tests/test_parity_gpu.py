@@ -52,6 +52,8 @@ SMALL_SHAPES = [
     (257, 264, 288, 4),    # m_pad = 260: one row past a 256-row tile
     (512, 448, 256, 2),    # whole 256 x 224 tiles (no bounds checks)
     (512, 512, 512, 4),    # whole 256 x 256 tiles (no bounds checks)
+    (4100, 4104, 272, 2),  # 289 tiles of 256 x 256 > 256 workgroups: some run two tiles; ragged m, n, K
+    (8192, 3584, 128, 2),  # 512 tiles of 256 x 224: every workgroup runs two tiles
 ]
 
 
@@ -198,7 +200,7 @@ def test_received_chunk_end_to_end(wid):
 
 # ------------------------------------------------------------------------ w8a8
 W8A8_SHAPES = [(64, 512, 256, 2), (5, 24, 32, 2), (17, 40, 64, 8), (300, 520, 672, 2), (257, 264, 272, 4),
-               (512, 448, 256, 2), (512, 512, 512, 4)]
+               (512, 448, 256, 2), (512, 512, 512, 4), (4100, 4104, 160, 2)]
 
 
 def _w8a8_inputs(m, n, k, seed):
