@@ -17,6 +17,9 @@ Parity status of each function (what pins it lives in tests/test_oracle_pins.py)
                          scale invariance, zero row, hand-worked golden
   w8a8_rows              pinned: numpy int64 GEMM, sign symmetry, numpy float32
                          dequant in the same operation order
+  quant_per_token        pinned: exact rational nearest-integer bound, absmax code
+                         +-127, power-of-two scale invariance, negation symmetry,
+                         zero row, hand-worked ties-to-even golden
   f64_to_bf16            pinned: exact rational nearest-even search
 """
 from __future__ import annotations
@@ -73,6 +76,8 @@ def load(path: str):
                                            ctypes.c_float, _p, _p, _p, _p]
     L.orc_w8a8_rows.restype = ctypes.c_int
     L.orc_w8a8_rows.argtypes = [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+    L.orc_quant_per_token.restype = ctypes.c_int
+    L.orc_quant_per_token.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p]
     L.orc_num_threads.restype = ctypes.c_int
     L.orc_set_num_threads.argtypes = [ctypes.c_int]
     return L
@@ -223,3 +228,20 @@ def w8a8_rows(xq: np.ndarray, sx: np.ndarray, wq: np.ndarray, sw: np.ndarray, m:
     if rc != 0:
         raise RuntimeError(f"orc_w8a8_rows failed: {rc}")
     return out, acc
+
+
+def quant_per_token(x: np.ndarray, rows: int | None = None):
+    """Per-token dynamic int8 quantisation of bf16 rows (reading R6).
+
+    x: uint16 bf16 bits [m, k].  Returns (xq int8 [r, k], sx float32 [r]) for the
+    first ``rows`` rows (default all).
+    """
+    ldx = _check2d(x, np.uint16, "x")
+    m = x.shape[0] if rows is None else min(int(rows), x.shape[0])
+    k = x.shape[1]
+    xq = np.empty((m, k), dtype=np.int8)
+    sx = np.empty((m,), dtype=np.float32)
+    rc = lib().orc_quant_per_token(_ptr(x), ldx, m, k, _ptr(xq), k, _ptr(sx))
+    if rc != 0:
+        raise RuntimeError(f"orc_quant_per_token failed: {rc}")
+    return xq, sx

@@ -36,7 +36,10 @@
  *       (pass 1+w for the Gemma form);
  *   R5  w8a8: exact integer dot product (int64 here, must fit int32), then the
  *       dequantisation (float(acc) * s_x[m]) * s_w[n] done as two fp32
- *       multiplies in that order, then bf16 round-to-nearest-even of the fp32.
+ *       multiplies in that order, then bf16 round-to-nearest-even of the fp32;
+ *   R6  per-token dynamic int8 quantisation of the activation: scale = row
+ *       absmax / 127 in fp32, code = round-to-nearest-even of x / scale in fp32,
+ *       clamped to [-127, 127]; an all-zero row has scale 0 and codes 0.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  * OpenMP only splits independent output rows across threads; every dot
@@ -245,6 +248,52 @@ int orc_w8a8_rows(const int8_t *xq, int64_t ldx, const float *sx,
     }
     if (bad) return ORC_ERR_ARG;
     return ovf ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+/* ------------------------------------------- per-token dynamic int8 quantiser
+ * [FC1] review thread, RowParallelLinear forward: on the w8a8_dynamic path the
+ * (already sequence-scattered) bf16 activation is quantised before the int8
+ * matmul ("dynamic" = the activation scale is computed from the data at run
+ * time, one scale per token row, while the weight carries a fixed per-channel
+ * weight_scale).  The page names the step but not its arithmetic; reading R6:
+ *
+ *   amax[r] = max_k |x[r, k]|                       (exact: bf16 -> fp32)
+ *   sx[r]   = amax[r] / 127                          one fp32 division, nearest-even
+ *   xq[r,k] = clamp(rint(x[r,k] / sx[r]), -127, 127) fp32 division, then round to
+ *                                                    the nearest integer, ties to even
+ *   a row of zeros (amax = 0): sx = 0 and every code 0 (the quotient is undefined).
+ *
+ * Symmetric, so the int8 code -128 never occurs.  Codes are integers decided
+ * in fp32, the precision the reading fixes, so both this oracle and the GPU
+ * take the same decision.  Inputs must be finite.                            */
+int orc_quant_per_token(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                        int8_t *xq, int64_t ldq, float *sx)
+{
+    if (!x || !xq || !sx) return ORC_ERR_ARG;
+    if (m < 0 || k < 0 || ldx < k || ldq < k) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < m; ++r) {
+        const uint16_t *xr = x + r * ldx;
+        float amax = 0.0f;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            float a = fabsf((float)orc_bf16_to_f64(xr[kk]));   /* exact */
+            if (a > amax) amax = a;
+        }
+        volatile float s = amax / 127.0f;
+        sx[r] = s;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            int8_t q = 0;
+            if (amax > 0.0f) {
+                volatile float t = (float)orc_bf16_to_f64(xr[kk]) / s;
+                float v = nearbyintf(t);                        /* ties to even */
+                if (v > 127.0f) v = 127.0f;
+                if (v < -127.0f) v = -127.0f;
+                q = (int8_t)v;
+            }
+            xq[r * ldq + kk] = q;
+        }
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------------ plumbing */

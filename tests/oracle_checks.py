@@ -310,6 +310,82 @@ def check_w8a8_overflow(orc):
     raise AssertionError("int32 overflow not reported")
 
 
+# ------------------------------------------------------- per-token quantiser
+def _f32_nearest(v: Fraction) -> np.float32:
+    """The float32 nearest to an exact rational (ties to even), by neighbour search."""
+    f = np.float32(float(v))
+    best = None
+    for c in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        d = abs(Fraction(float(c)) - v)
+        if best is None or d < best[0] or (d == best[0] and (int(c.view(np.uint32)) & 1) == 0):
+            best = (d, c)
+    return np.float32(best[1])
+
+
+def _quant_rows_exact(x_bits: np.ndarray):
+    """Exact-rational evaluation of the quantiser's reading, element by element."""
+    codes = np.zeros(x_bits.shape, dtype=np.int64)
+    scales = np.zeros(x_bits.shape[0], dtype=np.float32)
+    for r in range(x_bits.shape[0]):
+        vals = [bf16_value(b) for b in x_bits[r]]
+        amax = max(abs(v) for v in vals)
+        s = _f32_nearest(amax / 127)
+        scales[r] = s
+        if amax == 0:
+            continue
+        for j, v in enumerate(vals):
+            q = _f32_nearest(v / Fraction(float(s)))
+            codes[r, j] = max(-127, min(127, round(Fraction(float(q)))))   # half to even
+    return codes, scales
+
+
+def _quant_test_rows(rng) -> np.ndarray:
+    rows = []
+    for scale in [1.0, 1e-3, 3.0e4, 2.0 ** -120, 2.0 ** -130, 1.0e36]:
+        z = rng.standard_normal((3, 40)).astype(np.float32) * np.float32(scale)
+        rows.append(z)
+    z = rng.standard_normal((2, 40)).astype(np.float32)
+    z[0, 0] = 9.0                 # absmax first
+    z[1, -1] = -9.0               # absmax last, negative
+    rows.append(z)
+    return _bits(np.concatenate(rows))
+
+
+def check_quant_exact(orc):
+    """Brute force: every scale is the fp32 nearest to absmax/127 and every code is
+    the half-to-even integer of the fp32 nearest to x/scale (exact rationals)."""
+    x = _quant_test_rows(np.random.default_rng(91))
+    xq, sx = orc.quant_per_token(x)
+    want_q, want_s = _quant_rows_exact(x)
+    assert np.array_equal(sx.view(np.uint32), want_s.view(np.uint32))
+    assert np.array_equal(xq.astype(np.int64), want_q)
+
+
+def check_quant_properties(orc):
+    """Closed-form facts of a symmetric per-row quantiser: the absmax element maps to
+    +-127, every code is within half a step, negation and power-of-two scaling."""
+    rng = np.random.default_rng(92)
+    x = _bits(rng.standard_normal((64, 300)).astype(np.float32))
+    xq, sx = orc.quant_per_token(x)
+    xv = synth.bf16_decode(x).astype(np.float64)
+    i = np.argmax(np.abs(xv), axis=1)
+    assert np.array_equal(xq[np.arange(64), i].astype(np.int64), np.sign(xv[np.arange(64), i]) * 127)
+    err = np.abs(xv - xq.astype(np.float64) * sx[:, None].astype(np.float64))
+    assert np.all(err <= sx[:, None] * (0.5 + 1e-5))
+    assert xq.min() >= -127
+    xn, sn = orc.quant_per_token(x ^ np.uint16(0x8000))
+    assert np.array_equal(sn, sx) and np.array_equal(xn.astype(np.int64), -xq.astype(np.int64))
+    for j in (-20, 9):
+        xs = _bits(xv.astype(np.float32) * np.float32(2.0 ** j))
+        q2, s2 = orc.quant_per_token(xs)
+        assert np.array_equal(q2, xq) and np.array_equal(s2, sx * np.float32(2.0 ** j))
+    xz = x.copy()
+    xz[5] = 0
+    q0, s0 = orc.quant_per_token(xz)
+    assert s0[5] == 0 and not q0[5].any()
+    assert np.array_equal(q0[:5], xq[:5]) and np.array_equal(q0[6:], xq[6:])
+
+
 # ----------------------------------------------------------------------- golden
 def check_golden(orc):
     with open(GOLDEN) as f:
@@ -336,6 +412,10 @@ def check_golden(orc):
                              np.asarray(q["wq"], np.int8), np.asarray(q["sw"], np.float32), 1)
     assert np.array_equal(acc, np.asarray(q["acc"], np.int32))
     assert np.array_equal(synth.bf16_decode(out), np.asarray(q["out"], np.float32))
+    q = g["quant_per_token"]
+    xq, sx = orc.quant_per_token(_bits(q["x"]))
+    assert np.array_equal(xq, np.asarray(q["codes"], np.int8))
+    assert np.array_equal(sx, np.asarray(q["scale"], np.float32))
 
 
 ALL_CHECKS = [
@@ -343,5 +423,5 @@ ALL_CHECKS = [
     check_partial_one_hot, check_partial_small_integers, check_partial_padding_and_chunks,
     check_reduce_bruteforce, check_rms_invariant, check_unit_rms_and_scale_invariance,
     check_zero_row_and_tp1, check_integer_partials_exact, check_w8a8, check_w8a8_overflow,
-    check_golden,
+    check_quant_exact, check_quant_properties, check_golden,
 ]

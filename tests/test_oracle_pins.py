@@ -3,8 +3,10 @@
 The second half plants plausible mistakes in copies of the oracle's C source
 (a dropped term, a wrong sign, a transposed operand, a wrong mean, eps outside
 the root, ties rounded away from zero, a missing subnormal clamp, a dropped
-residual, a reordered dequantisation), compiles each copy with gcc and checks
-that at least one pin fails for every one of them.
+residual, a reordered dequantisation, a quantiser that rounds ties away from
+zero, truncates, divides by 128, drops the absolute value or the last column,
+or gives a zero row scale 1), compiles each copy with gcc and checks that at
+least one pin fails for every one of them.
 """
 import os
 import shutil
@@ -62,6 +64,15 @@ MUTANTS = [
     ("dequant_scales_multiplied_first",
      "volatile float v = u * sw[j];",
      "volatile float v = t * (((r < m) ? sx[r] : 0.0f) * sw[j]);"),
+    ("quant_ties_away_from_zero", "float v = nearbyintf(t);", "float v = roundf(t);"),
+    ("quant_scale_over_128", "volatile float s = amax / 127.0f;", "volatile float s = amax / 128.0f;"),
+    ("quant_absmax_without_abs", "float a = fabsf((float)orc_bf16_to_f64(xr[kk]));",
+     "float a = (float)orc_bf16_to_f64(xr[kk]);"),
+    ("quant_absmax_skips_last_column", "for (int64_t kk = 0; kk < k; ++kk) {\n            float a",
+     "for (int64_t kk = 0; kk + 1 < k; ++kk) {\n            float a"),
+    ("quant_zero_row_scale_one", "volatile float s = amax / 127.0f;",
+     "volatile float s = amax > 0.0f ? amax / 127.0f : 1.0f;"),
+    ("quant_truncates", "float v = nearbyintf(t);", "float v = truncf(t);"),
     ("w8a8_sign_of_weight",
      "s += (int64_t)xr[kk] * (int64_t)wr[kk];",
      "s += (int64_t)xr[kk] * (int64_t)(kk == 0 ? -wr[kk] : wr[kk]);"),
