@@ -1,6 +1,7 @@
 """Benchmark of the row-parallel matmul + reduce hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill|long_prefill|w8a8|decode|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload prefill|long_prefill|w8a8|w8a8_dynamic|decode|tiny]
 
 One step is one pass of the path for one tensor-parallel rank, on synthetic
 inputs already resident in HBM:
@@ -10,11 +11,13 @@ inputs already resident in HBM:
   2. rpl_reduce_chunk_rmsnorm on the chunk the rank receives: its own chunk
      partial + the peers' chunk partials (data that arrives from the other
      ranks, produced before timing) -> residual add -> RMSNorm.
-A model layer runs the bf16 or the w8a8 partial, not both, so each precision is
-its own path.  The default run times the bf16 prefill down_proj share
+The w8a8_dynamic path starts one step earlier, from the bf16 activation:
+rpl_quant_per_token makes the int8 codes and per-token scales that the int8
+partial consumes.  A model layer runs the bf16 or the w8a8 partial, not both,
+so each precision is its own path.  The default run times the bf16 prefill down_proj share
 (M=4096, K_full=18944 over TP=2, N=3584) as the main step, and in the same run
 the w8a8 twin, the decode o_proj share and the TP=8 long-prefill share as side
-steps.  Every step cycles through several copies of its inputs (more than
+steps (w8a8 both from int8 inputs and from the bf16 activation).  Every step cycles through several copies of its inputs (more than
 twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
@@ -40,17 +43,23 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_I8_TOPS = 5033.2       # dense int8 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["gemm_nt.h", "gemm_bf16.hip", "gemm_w8a8.hip", "reduce_rmsnorm.hip", "rpl_device.h"]
-WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5}
+# the sources each kernel is built from (its stored HBM traffic is valid while they are unchanged)
+KERNEL_SOURCES = {
+    "partial_bf16": ["gemm_nt.h", "gemm_bf16.hip", "rpl_device.h"],
+    "partial_w8a8": ["gemm_nt.h", "gemm_w8a8.hip", "rpl_device.h"],
+    "reduce_rmsnorm": ["reduce_rmsnorm.hip", "rpl_device.h"],
+    "quant_per_token": ["quant_per_token.hip", "rpl_device.h"],
+}
+WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "row_matmul_reduce_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -63,18 +72,19 @@ def load_traffic(kernel_key: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f).get(f"{kernel_key}@{workload}")
-    if not rec or rec.get("source_sha256_16") != kernel_source_hash():
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(kernel_key):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
 class Path:
-    """One rank's step (partial + received-chunk reduce/RMSNorm) on several input sets."""
+    """One rank's step ([quantiser +] partial + received-chunk reduce/RMSNorm) on several input sets."""
 
-    def __init__(self, wl, torch, rpl, copies: int):
+    def __init__(self, wl, torch, rpl, copies: int, dynamic: bool = False):
         from row_matmul_reduce_amd import synth
         self.wl, self.torch, self.rpl = wl, torch, rpl
         self.w8 = wl.kind == "w8a8"
+        self.dyn = self.w8 and dynamic
         t0 = time.perf_counter()
         mc = wl.m_chunk
         dev = torch.device("cuda")
@@ -86,7 +96,15 @@ class Path:
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
         base = {"res": bf(synth.residual_chunk(wl)), "gam": bf(synth.gamma(wl))}
-        if self.w8:
+        if self.dyn:
+            wq, sw = synth.w8a8_weight(wl, 0)
+            base.update(x=bf(synth.x_shard(wl, 0)), wq=up(wq), sw=up(sw))
+            peers = []
+            for s in range(1, wl.tp):
+                pwq, psw = synth.w8a8_weight(wl, s)
+                pq, psx = rpl.rpl_quant_per_token(bf(synth.x_shard(wl, s, rows=mc)))
+                peers.append(rpl.rpl_w8a8_partial(pq, psx, up(pwq), up(psw), 1))
+        elif self.w8:
             xq, sx, wq, sw = synth.w8a8_inputs(wl, shard=0)
             base.update(xq=up(xq), sx=up(sx), wq=up(wq), sw=up(sw))
             peers = []
@@ -107,13 +125,23 @@ class Path:
         self.p = torch.empty((wl.m_pad, wl.n), dtype=torch.bfloat16, device=dev)
         self.y = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
         self.ro = torch.empty((mc, wl.n), dtype=torch.bfloat16, device=dev)
-        self.names = ["partial_w8a8" if self.w8 else "partial_bf16", "reduce_rmsnorm"]
+        if self.dyn:
+            self.xq = torch.empty((wl.m, wl.k_shard), dtype=torch.int8, device=dev)
+            self.sx = torch.empty((wl.m,), dtype=torch.float32, device=dev)
+        self.pname = "partial_w8a8" if self.w8 else "partial_bf16"
+        self.names = (["quant_per_token"] if self.dyn else []) + [self.pname, "reduce_rmsnorm"]
+        self.stages = ([self.quant] if self.dyn else []) + [self.partial, self.reduce]
         torch.cuda.synchronize()
         log(f"{wl.name}: inputs ready in {time.perf_counter() - t0:.1f} s, {len(self.sets)} copies x "
             f"{self.set_bytes / 1e6:.0f} MB")
 
+    def quant(self, d):
+        self.rpl.rpl_quant_per_token(d["x"], xq=self.xq, x_scale=self.sx)
+
     def partial(self, d):
-        if self.w8:
+        if self.dyn:
+            self.rpl.rpl_w8a8_partial(self.xq, self.sx, d["wq"], d["sw"], self.wl.tp, out=self.p)
+        elif self.w8:
             self.rpl.rpl_w8a8_partial(d["xq"], d["sx"], d["wq"], d["sw"], self.wl.tp, out=self.p)
         else:
             self.rpl.rpl_partial(d["x"], d["w"], self.wl.tp, out=self.p)
@@ -124,15 +152,12 @@ class Path:
 
     def step(self, i, evs=None):
         d = self.sets[i % len(self.sets)]
-        if evs is not None:
-            evs[0][0].record()
-        self.partial(d)
-        if evs is not None:
-            evs[0][1].record()
-            evs[1][0].record()
-        self.reduce(d)
-        if evs is not None:
-            evs[1][1].record()
+        for j, fn in enumerate(self.stages):
+            if evs is not None:
+                evs[j][0].record()
+            fn(d)
+            if evs is not None:
+                evs[j][1].record()
 
     def run_graphs(self, steps: int, warmup: int):
         """Small (decode) paths: the host launch cost exceeds the kernels, so time HIP graphs
@@ -165,9 +190,8 @@ class Path:
         g_step.replay()          # exactly `steps` steps
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern = {self.names[0]: per_launch_us(capture(lambda d, i: self.partial(d))),
-                self.names[1]: per_launch_us(capture(lambda d, i: self.reduce(d)))}
-        return wall * 1e3 / steps, kern, kern[self.names[0]]
+        kern = {nm: per_launch_us(capture(lambda d, i, fn=fn: fn(d))) for nm, fn in zip(self.names, self.stages)}
+        return wall * 1e3 / steps, kern, kern[self.pname]
 
     def run(self, steps: int, warmup: int):
         """Time `steps` steps after `warmup`: wall ms per step, per-kernel HIP event means (us),
@@ -196,7 +220,7 @@ class Path:
 
     def kernels_report(self, kern, period):
         wl = self.wl
-        pn, rn = self.names
+        pn, rn = self.pname, "reduce_rmsnorm"
         flop, pbytes, rbytes = wl.gemm_flops(), wl.partial_bytes(), wl.reduce_bytes()
         pu = kern[pn]
         peak = PEAK_I8_TOPS if self.w8 else PEAK_BF16_TFLOPS
@@ -210,6 +234,10 @@ class Path:
         ru = kern[rn]
         rep[rn] = {"us": ru, "bytes": rbytes, "GB/s": rbytes / (ru * 1e-6) / 1e9}
         rep[rn]["frac_hbm"] = rep[rn]["GB/s"] / PEAK_HBM_GBS
+        if self.dyn:
+            qu, qb = kern["quant_per_token"], wl.quant_bytes()
+            rep["quant_per_token"] = {"us": qu, "bytes": qb, "GB/s": qb / (qu * 1e-6) / 1e9,
+                                      "frac_hbm": qb / (qu * 1e-6) / 1e9 / PEAK_HBM_GBS}
         return rep
 
 
@@ -272,7 +300,8 @@ def main():
     ap.add_argument("--workload", default="prefill", choices=list(WORKLOAD_IDS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-side", action="store_true", help="skip the side paths (w8a8, decode, long prefill)")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side paths (w8a8, w8a8_dynamic, decode, long prefill)")
     ap.add_argument("--copies", type=int, default=0,
                     help="input sets cycled through (0: enough to exceed twice the 256 MB MALL)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -302,12 +331,12 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}}))
         return
     wl = synth.WORKLOADS[WORKLOAD_IDS[args.workload]]
-    path = Path(wl, torch, rpl, args.copies)
+    path = Path(wl, torch, rpl, args.copies, dynamic=args.workload == "w8a8_dynamic")
     small = wl.m_pad <= 16
     runner = path.run_graphs if small else path.run
     ms_per_step, kern, period = runner(args.steps, args.warmup)
     kernels = path.kernels_report(kern, period)
-    pn = path.names[0]
+    pn = path.pname
     if small:  # decode: bound by the weight stream
         value, unit = (wl.partial_bytes() + wl.reduce_bytes()) / (ms_per_step * 1e-3) / 1e9, "GB/s"
         roofline = {"bound": "hbm", "kernel": pn, "achieved": kernels[pn]["GB/s"], "peak": PEAK_HBM_GBS,
@@ -328,9 +357,9 @@ def main():
 
     side = {}
     if not args.no_side and args.workload == "prefill":
-        for key in ("w8a8", "decode", "long_prefill"):
+        for key in ("w8a8", "w8a8_dynamic", "decode", "long_prefill"):
             swl = synth.WORKLOADS[WORKLOAD_IDS[key]]
-            sp = Path(swl, torch, rpl, args.copies)
+            sp = Path(swl, torch, rpl, args.copies, dynamic=key == "w8a8_dynamic")
             if swl.m_pad <= 16:
                 s_ms, s_kern, s_period = sp.run_graphs(200, 3)
             else:
@@ -353,7 +382,7 @@ def main():
                    "input_sets_rotated": sets_used},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "side": side,
         "library_reference": reference,
-        "kernel_sources_sha256_16": kernel_source_hash(),
+        "kernel_sources_sha256_16": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
 

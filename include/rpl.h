@@ -185,10 +185,40 @@ rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
                             int64_t m, int64_t n, int64_t k, int32_t tp,
                             void *stream);
 
+/*
+ * rpl_quant_per_token -- per-token dynamic int8 quantisation of a bf16
+ * activation, the producer of rpl_w8a8_partial's xq and x_scale.
+ *
+ * [FC1] review thread (RowParallelLinear forward on the w8a8_dynamic path):
+ * the scattered activation is quantised at run time before the int8 matmul.
+ * The page does not spell out the arithmetic; the symmetric per-row form is
+ * used, with every operation in fp32:
+ *   amax[r]    = max_k |x[r, k]|
+ *   x_scale[r] = amax[r] / 127                       (IEEE division, nearest-even)
+ *   xq[r, k]   = clamp(rint(x[r, k] / x_scale[r]), -127, 127)
+ * rint rounds half to even; an all-zero row gets x_scale 0 and all codes 0.
+ * Codes are exact functions of the input (correctly rounded divisions).  Inputs
+ * must be finite: a row holding Inf or NaN gets unspecified codes and scale.
+ *
+ * x        [m, k] bf16, row stride ldx >= k
+ * xq       [m, k] int8, row stride ldq >= k (columns k..ldq-1 are not written)
+ * x_scale  [m] fp32
+ * xq and x_scale must not overlap each other or x.
+ *
+ * RPL_ERR_NULL        m > 0 and x, xq or x_scale is NULL
+ * RPL_ERR_INVALID     m < 0, k < 1, ldx < k, ldq < k, overlaps
+ * RPL_ERR_UNSUPPORTED k, ldx or ldq not a multiple of 8; x or xq not 16-byte
+ *                     aligned or x_scale not 4-byte aligned; m or k >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx,
+                               int8_t *xq, int64_t ldq, float *x_scale,
+                               int64_t m, int64_t k, void *stream);
+
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 1.0. */
+/* Library ABI version: (major << 16) | minor.  Currently 1.1. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

@@ -12,6 +12,7 @@ the library is missing, every call raises.
                                                -> (y, residual_out)
     rpl_w8a8_partial(xq, x_scale, wq, w_scale, tp, want_acc=False)
                                                -> out (, acc)
+    rpl_quant_per_token(x)                     -> (xq int8, x_scale fp32)
 """
 from __future__ import annotations
 
@@ -49,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.rpl_reduce_chunk_rmsnorm.argtypes = [_p, _i32, _i64, _i64, _p, _p, ctypes.c_float, _p, _p, _p]
         L.rpl_w8a8_partial.restype = ctypes.c_int
         L.rpl_w8a8_partial.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
+        L.rpl_quant_per_token.restype = ctypes.c_int
+        L.rpl_quant_per_token.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
         L.rpl_status_string.argtypes = [ctypes.c_int]
         L.rpl_version.restype = ctypes.c_int32
@@ -194,5 +197,28 @@ def rpl_w8a8_partial(xq, x_scale, wq, w_scale, tp: int, out=None, acc=None, want
     return (out, acc) if acc is not None else out
 
 
-__all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_status_string", "rpl_version",
+def rpl_quant_per_token(x, xq=None, x_scale=None, stream=None):
+    """Per-token dynamic int8 quantisation of a bf16 [m, k] activation.
+
+    Returns (xq int8 [m, k], x_scale fp32 [m]), the operands of rpl_w8a8_partial.
+    """
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _dev(xq, "xq", torch.int8, 2)
+    _dev(x_scale, "x_scale", torch.float32, 1)
+    if tuple(xq.shape) != (m, k) or x_scale.shape[0] != m:
+        raise ValueError(f"xq must be [{m}, {k}] and x_scale [{m}]")
+    st = lib().rpl_quant_per_token(x.data_ptr(), _ld(x), xq.data_ptr(), _ld(xq), x_scale.data_ptr(), m, k,
+                                   _stream(x, stream))
+    _check("rpl_quant_per_token", st)
+    return xq, x_scale
+
+
+__all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
+           "rpl_status_string", "rpl_version",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

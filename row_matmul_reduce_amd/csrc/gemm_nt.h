@@ -50,6 +50,7 @@
 namespace rpl {
 
 constexpr int KT_BYTES = 128;  // bytes of K staged per step, per operand row
+constexpr int NUM_CU = 256;  // MI355X compute units
 constexpr int NUM_XCD = 8;
 constexpr int PF_BYTES = 256;  // LDS sink of the prefetch loads (64 lanes x 4 bytes)
 // Largest operand row stride (bytes) the 32-bit buffer offsets of a 256-row tile can address.
@@ -263,6 +264,20 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
 }
 
 // Grid of the persistent tile loop.
-__host__ __device__ inline int persistent_grid(int tiles) { return tiles < 256 ? tiles : 256; }
+__host__ __device__ inline int persistent_grid(int tiles) { return tiles < NUM_CU ? tiles : NUM_CU; }
+
+// Output tile width for the 256-row tile engine: 224 when it divides n and
+// packs the grid into fewer/fuller waves of workgroups over the 256 CUs than
+// 256 does, else 256.
+inline int pick_tile_n(int m_pad, int n) {
+    auto fill = [&](int bn) {
+        const long tiles = (long)((m_pad + 255) / 256) * ((n + bn - 1) / bn);
+        const long waves = (tiles + NUM_CU - 1) / NUM_CU;
+        const double useful = (double)m_pad * n;
+        return useful / ((double)waves * NUM_CU * 256.0 * bn);  // useful share of the issued tile waves
+    };
+    if (n % 224 == 0 && fill(224) > fill(256) + 1e-9) return 224;
+    return 256;
+}
 
 }  // namespace rpl

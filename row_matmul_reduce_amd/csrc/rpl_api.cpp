@@ -131,6 +131,21 @@ rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
                                                   (int)n, (int)k, static_cast<hipStream_t>(stream)));
 }
 
+rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx, int8_t *xq, int64_t ldq, float *x_scale, int64_t m,
+                               int64_t k, void *stream) {
+    if (m != 0 && (!x || !xq || !x_scale)) return RPL_ERR_NULL;
+    if (m < 0 || k < 1 || ldx < k || ldq < k) return RPL_ERR_INVALID;
+    const int64_t xb = span(m, k, ldx, 2), qb = span(m, k, ldq, 1), sb = span(1, m, m, 4);
+    if (overlap(xq, qb, x, xb) || overlap(x_scale, sb, x, xb) || overlap(xq, qb, x_scale, sb))
+        return RPL_ERR_INVALID;
+    if (k % 8 || ldx % 8 || ldq % 8) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return RPL_ERR_UNSUPPORTED;
+    if (m > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    return launch_status(rpl::launch_quant_per_token(x, ldx, xq, ldq, x_scale, (int)m, (int)k,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 const char *rpl_status_string(rpl_status s) {
     switch (s) {
         case RPL_OK: return "RPL_OK";
@@ -142,6 +157,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (1 << 16) | 0; }
+int32_t rpl_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

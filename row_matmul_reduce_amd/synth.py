@@ -68,6 +68,10 @@ class Workload:
                     + 2 * self.m_pad * self.n)
         return 2 * (self.m * self.k_shard + self.n * self.k_shard + self.m_pad * self.n)
 
+    def quant_bytes(self) -> int:
+        """Algorithmic HBM bytes of the per-token quantiser of the rank's activation."""
+        return 3 * self.m * self.k_shard + 4 * self.m
+
     def reduce_bytes(self) -> int:
         """Algorithmic HBM bytes of the chunk reduce + residual + RMSNorm."""
         mc, n = self.m_chunk, self.n
@@ -176,6 +180,61 @@ def w8a8_inputs(wl: Workload, rows: int | None = None, shard: int = 0):
     sx = np.where(sx > 0, sx, np.float32(1.0)).astype(np.float32)
     q = np.rint(xf / sx[:, None])
     xq = np.clip(q, -127, 127).astype(np.int8)
+    wq, sw = w8a8_weight(wl, shard)
+    return np.ascontiguousarray(xq), sx, wq, sw
+
+
+def w8a8_weight(wl: Workload, shard: int = 0):
+    """Rank `shard`'s int8 weight [n, k_shard] (uniform over -127..127) and its
+    per-channel fp32 scale [n] ~ U(1e-3, 1e-2)."""
     wq = _rng(wl, T_W, shard).integers(-127, 128, (wl.n, wl.k_shard), dtype=np.int8)
     sw = _rng(wl, T_WSCALE, shard).uniform(1e-3, 1e-2, wl.n).astype(np.float32)
-    return np.ascontiguousarray(xq), sx, np.ascontiguousarray(wq), sw
+    return np.ascontiguousarray(wq), sw
+
+
+def quant_test_rows(m: int, k: int, seed: int) -> np.ndarray:
+    """bf16 rows [m, k] for the per-token quantiser: N(0,1) rows scaled by
+    10^U(-30, 30), with special rows cycled in: all zero, bf16-subnormal
+    magnitudes, near the bf16 maximum, half-integers up to 126.5 with absmax
+    127 (exact ties), a single non-zero element, a constant row, a run of
+    consecutive bf16 codes (every value of the run), and small-significand
+    values under a small-significand absmax (many quotients at or next to
+    half-integers)."""
+    rng = np.random.default_rng([seed, 7])
+    z = rng.standard_normal((m, k), dtype=np.float32)
+    mag = (10.0 ** rng.uniform(-30, 30, (m, 1))).astype(np.float32)
+    v = z * mag
+    for r in range(m):
+        kind = r % 9
+        if kind == 1:
+            v[r] = 0.0
+        elif kind == 2:
+            v[r] = z[r] * np.float32(2.0 ** -130)
+        elif kind == 3:
+            v[r] = np.clip(z[r], -1.5, 1.5) * np.float32(2.0e38)
+        elif kind == 4:
+            v[r] = rng.integers(-127, 127, k).astype(np.float32) + np.float32(0.5)
+            v[r, rng.integers(0, k)] = -127.0
+        elif kind == 5:
+            v[r] = 0.0
+            v[r, rng.integers(0, k)] = z[r, 0]
+        elif kind == 6:
+            v[r] = np.float32(-0.375)
+    b = bf16_bits(v)
+    for r in range(7, m, 9):
+        # every bf16 value of a run of consecutive codes below a random start, signs alternating
+        start = int(bf16_bits(np.abs(v[r, :1]))[0])
+        run = np.maximum(start - np.arange(k), 0).astype(np.uint16)
+        run[1::2] |= np.uint16(0x8000)
+        b[r] = run
+    for r in range(8, m, 9):
+        # small-significand values: absmax c * 2^e (c odd, 1..15), elements (odd j) * 2^(e - q)
+        e = int(rng.integers(-40, 40))
+        c = float(rng.choice([1, 3, 5, 7, 9, 11, 13, 15]))
+        j = rng.integers(0, 128, k) * 2 + 1
+        q = rng.integers(4, 12, k)
+        row = (j * np.exp2(e - q.astype(np.float64))).astype(np.float32)
+        row = np.minimum(row, np.float32(c * 2.0 ** e)) * np.where(rng.random(k) < 0.5, -1, 1).astype(np.float32)
+        row[int(rng.integers(0, k))] = np.float32(c * 2.0 ** e)
+        b[r] = bf16_bits(row)
+    return b

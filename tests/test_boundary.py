@@ -28,9 +28,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(rpl_[a-z0-9_]+)\s*\(", src)))
 
 
-def test_header_declares_the_three_calls():
+def test_header_declares_the_path_calls():
     names = declared_functions()
-    for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_status_string", "rpl_version"):
+    for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
+              "rpl_status_string", "rpl_version"):
         assert f in names
 
 
@@ -49,7 +50,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (1 << 16)
+    assert rpl.rpl_version() == (1 << 16) | 1
 
 
 class Buf:
@@ -190,6 +191,40 @@ def test_w8a8_validation():
     assert w8a8_call(None, k, None, wq, k, sw, None, None, 0, n, k, tp) == OK
     for b in (XQ, SX, WQ, SW, O, A):
         assert b.untouched()
+
+
+def quant_call(x, ldx, xq, ldq, sx, m, k):
+    return rpl.lib().rpl_quant_per_token(x, ldx, xq, ldq, sx, m, k, None)
+
+
+def test_quant_validation():
+    m, k = 5, 64
+    X, Q, S = Buf(m * k * 2), Buf(m * k), Buf(m * 4)
+    x, q, sx = X.ptr, Q.ptr, S.ptr
+    cases = [
+        ((None, k, q, k, sx, m, k), NULL),
+        ((x, k, None, k, sx, m, k), NULL),
+        ((x, k, q, k, None, m, k), NULL),
+        ((x, k, q, k, sx, -1, k), INVALID),
+        ((x, k, q, k, sx, m, 0), INVALID),
+        ((x, 56, q, k, sx, m, k), INVALID),            # ldx < k
+        ((x, k, q, 56, sx, m, k), INVALID),            # ldq < k
+        ((x, k, x + 16, k, sx, m, k), INVALID),        # xq overlaps x
+        ((x, k, q, k, x + 64, m, k), INVALID),         # x_scale overlaps x
+        ((x, k, q, k, q + 32, m, k), INVALID),         # x_scale overlaps xq
+        ((x, 76, q, 76, sx, m, 68), UNSUP),            # k % 8
+        ((x, 68, q, k, sx, m, k), UNSUP),              # ldx % 8
+        ((x, k, q, 68, sx, m, k), UNSUP),              # ldq % 8
+        ((x + 8, k, q, k, sx, m, k), UNSUP),
+        ((x, k, q + 8, k, sx, m, k), UNSUP),
+        ((x, k, q, k, sx + 2, m, k), UNSUP),
+        ((1 << 44, k, 1 << 45, k, 1 << 46, 1 << 31, k), UNSUP),   # m >= 2^31 (far-apart fake addresses)
+    ]
+    for args, want in cases:
+        assert quant_call(*args) == want, args
+    for b in (X, Q, S):
+        assert b.untouched()
+    assert quant_call(None, k, None, k, None, 0, k) == OK
 
 
 def test_binding_rejects_host_tensors():
