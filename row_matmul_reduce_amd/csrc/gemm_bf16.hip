@@ -39,13 +39,13 @@ struct Bf16Op {
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF>
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN)))
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 gemm_bf16_prefill_kernel(GemmShape g, uint16_t *out) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (BM + BN) * KT_BYTES + PF_BYTES];
     Bf16Op op{out, g.n};
-    gemm_nt_persistent<BM, BN, WM, WN, PRIO, PF>(g, op, smem);
+    gemm_nt_persistent<BM, BN, WM, WN, PRIO, PF, SCHED>(g, op, smem);
 }
 
 // ---------------------------------------------------------------- decode path
@@ -98,10 +98,10 @@ gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint1
 }
 
 // ---------------------------------------------------------------- launchers
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF>
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
 static hipError_t launch_prefill(const GemmShape &g, uint16_t *out, hipStream_t st) {
     const int nt = ((g.m_pad + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, PRIO, PF>), dim3(persistent_grid(nt)), dim3(64 * WM * WN), 0, st, g, out);
+    hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, PRIO, PF, SCHED>), dim3(persistent_grid(nt)), dim3(64 * WM * WN), 0, st, g, out);
     return hipGetLastError();
 }
 
@@ -114,8 +114,8 @@ hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w
     }
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),
                 ldx * 2, ldw * 2, m, m_pad, n, k * 2, 4};
-    if (pick_tile_n(m_pad, n) == 224) return launch_prefill<256, 224, 4, 2, false, 2>(g, out, st);
-    return launch_prefill<256, 256, 2, 4, true, 3>(g, out, st);
+    if (pick_tile_n(m_pad, n) == 224) return launch_prefill<256, 224, 4, 2, false, 3, 2>(g, out, st);
+    return launch_prefill<256, 256, 2, 4, true, 3, 3>(g, out, st);
 }
 
 }  // namespace rpl

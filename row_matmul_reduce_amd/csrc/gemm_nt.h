@@ -106,7 +106,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
 // so a workgroup stays on one XCD's tile range).  A tile's first DMA is issued before
 // the previous tile's results are stored, so the stores overlap that load.
 // smem: 2 * (BM + BN) * KT_BYTES + PF_BYTES bytes of LDS.
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF, class Op>
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED, class Op>
 __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op &op, uint8_t *smem) {
     constexpr int NW = WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;
@@ -219,6 +219,11 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
         }
     };
 
+    // DMA instructions this wave issues per step (the fewest any wave issues: vmcnt
+    // immediates below must not exceed any wave's own count).
+    constexpr int DMA_MIN = GA / NW + GB / NW;
+    constexpr int DMA_MAX = (GA + NW - 1) / NW + (GB + NW - 1) / NW;
+
     Frag xa[FM], wa[FN], xb[FM], wb[FN];
     int pm0 = 0, pn0 = 0;
     bool have_prev = false;
@@ -228,27 +233,53 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
         const int m0 = tm * BM, n0 = tn * BN;
         rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
         rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
-        for (int d = 1; d < PF; ++d) prefetch(d);
-        issue(0, s0);  // every wave passed the previous tile's last barrier: no LDS reads remain
+        for (int d = 2; d < PF; ++d) prefetch(d);
+        issue(0, s0);  // every wave passed the previous tile's last barrier: no LDS reads it needs remain
         if (have_prev) store_tile(pm0, pn0);
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
             for (int b = 0; b < FN; ++b) acc[a][b] = Op::zero();
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (ksteps > 1) {
+            issue(1, s1);  // stays in flight; everything older (step 0, the stores) must land
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(DMA_MIN) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        }
         if (PRIO) __builtin_amdgcn_s_setprio(1);
         load_frags(s0, 0, xa, wa);
         landed(xa, wa);
         uint8_t *cur = s0, *nxt = s1;
         for (int kt = 0; kt < ksteps; ++kt) {
-            const bool more = kt + 1 < ksteps;
-            if (more) issue(kt + 1, nxt);
             if (PF > 0) prefetch(kt + PF);  // past the end: out of range, reads nothing
             load_frags(cur, 1, xb, wb);
             mfmas(xa, wa);
-            barrier(xb, wb);
-            if (more) load_frags(nxt, 0, xa, wa);
+            barrier(xb, wb);  // step kt+1 has landed in nxt; nobody reads cur any more
+            // Second half: its MFMAs, the first-half fragment reads of step kt+1 and the DMA
+            // of step kt+2 into the buffer just released, interleaved one-for-one so the
+            // MFMA pipe never waits on instruction issue.  Both run unconditionally (one
+            // basic block to schedule): after the last step the reads fetch a buffer that
+            // is never used, and past the end the DMA offsets are out of range, which
+            // writes zeros into a buffer nobody reads before the next tile's own DMA
+            // (loads complete in issue order).
             mfmas(xb, wb);
+            load_frags(nxt, 0, xa, wa);
+            if (SCHED == 2) issue(kt + 2, cur);
+#pragma unroll
+            for (int i = 0; i < FM + FN; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            }
+            if (SCHED == 2) {
+#pragma unroll
+                for (int i = 0; i < DMA_MAX; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA load
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);  // the remaining MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            if (SCHED != 2 && kt + 2 < ksteps) issue(kt + 2, cur);
             landed(xa, wa);
             uint8_t *tmp = cur;
             cur = nxt;

@@ -43,18 +43,18 @@ struct W8a8Op {
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF>
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN)))
 __attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
 gemm_w8a8_kernel(GemmShape g, W8a8Op op) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (BM + BN) * KT_BYTES + PF_BYTES];
-    gemm_nt_persistent<BM, BN, WM, WN, PRIO, PF>(g, op, smem);
+    gemm_nt_persistent<BM, BN, WM, WN, PRIO, PF, SCHED>(g, op, smem);
 }
 
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF>
+template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
 static hipError_t launch_w8a8(const GemmShape &g, const W8a8Op &op, hipStream_t st) {
     const int nt = ((g.m_pad + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, PRIO, PF>), dim3(persistent_grid(nt)), dim3(64 * WM * WN), 0, st, g, op);
+    hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WM, WN, PRIO, PF, SCHED>), dim3(persistent_grid(nt)), dim3(64 * WM * WN), 0, st, g, op);
     return hipGetLastError();
 }
 
@@ -64,8 +64,8 @@ hipError_t launch_partial_w8a8(const int8_t *xq, int64_t ldx, const float *sx, c
     GemmShape g{reinterpret_cast<const uint8_t *>(xq), reinterpret_cast<const uint8_t *>(wq), ldx, ldw, m, m_pad, n,
                 k, 4};
     W8a8Op op{out, acc, sx, sw, m, n};
-    if (pick_tile_n(m_pad, n) == 224) return launch_w8a8<256, 224, 4, 2, false, 2>(g, op, st);
-    return launch_w8a8<256, 256, 2, 4, true, 3>(g, op, st);
+    if (pick_tile_n(m_pad, n) == 224) return launch_w8a8<256, 224, 4, 2, false, 3, 2>(g, op, st);
+    return launch_w8a8<256, 256, 2, 4, true, 3, 3>(g, op, st);
 }
 
 }  // namespace rpl
