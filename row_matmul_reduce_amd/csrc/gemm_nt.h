@@ -20,11 +20,14 @@
 // sits at chunk (c ^ (r & 7)), so the 16 rows one MFMA fragment read touches
 // fall on distinct banks (zero bank conflicts measured with rocprofv3).
 //
-// L2 prefetch.  Two buffers of LDS give the DMA of step k+1 only one step of
-// lead, less than the latency of HBM under load.  So each step also touches
-// the lines of step k+PF (PF = 2 or 3) once -- one 4-byte DMA per 128-byte line
-// into a 256-byte LDS sink that is never read -- so that the real DMA finds
-// them in L2.  The barrier waits for every load but that newest one.
+// L2 prefetch.  Two buffers of LDS give the DMA of step k+2 one step of lead,
+// less than the latency of HBM under load.  So each step also touches the
+// lines of step k+PF (PF = 3) -- one 4-byte DMA per 128-byte line into a
+// 256-byte LDS sink that is never read -- so that the real DMA finds them in
+// L2.  The workgroups of an XCD that share a row split its prefetch between
+// them, so each line is touched about once per XCD rather than once per
+// sharer (half the L2 requests of a per-workgroup prefetch).  The barrier
+// waits for every load but that newest one.
 //
 // Schedule.  Per K step each wave reads its fragments for the two 32-deep
 // halves of the step from LDS and issues its MFMAs.  The second half's
@@ -53,6 +56,7 @@ constexpr int KT_BYTES = 128;  // bytes of K staged per step, per operand row
 constexpr int NUM_CU = 256;  // MI355X compute units
 constexpr int NUM_XCD = 8;
 constexpr int PF_BYTES = 256;  // LDS sink of the prefetch loads (64 lanes x 4 bytes)
+constexpr int PF_SHARE_X = 8;  // workgroups of one XCD that share an activation row at a time
 // Largest operand row stride (bytes) the 32-bit buffer offsets of a 256-row tile can address.
 constexpr int64_t MAX_LD_BYTES = int64_t(1) << 23;
 
@@ -113,7 +117,7 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int GA = BM / 8, GB = BN / 8;  // 8-row (1 KB) groups per operand per step
     static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-    static_assert(BM % 64 == 0 && (BM + BN + 63) / 64 == NW, "one prefetch instruction per wave and operand");
+    static_assert(NW >= 2 && BM / PF_SHARE_X <= 64, "prefetch slices: activation rows on wave 0, weight rows on wave 1");
     using Frag = typename Op::Frag;
     using Acc = typename Op::Acc;
 
@@ -153,17 +157,26 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
             }
         }
     };
-    // L2 prefetch of step kt: wave w touches tile rows [64w, 64w + 64) (activation rows
-    // first, then weight rows), one lane per row.
+    // L2 prefetch of step kt.  The tiles an XCD runs at once form a band of group_m
+    // tile rows by about 8 tile columns (see tile_of_block), so 8 workgroups share each
+    // activation row and group_m share each weight row.  Each workgroup touches only its
+    // slice: activation rows [(tn % 8) * BM/8, +BM/8) on wave 0 and weight rows
+    // [(tm % group_m) * BN/group_m, +BN/group_m) on wave 1, one lane per row; the other
+    // waves issue an out-of-range load so that every wave has one prefetch in flight
+    // (the barrier's vmcnt counts on it).  A slice another workgroup misses only costs
+    // that line its lead; the DMA reads it regardless.
+    int tm = 0, tn = 0;
     auto prefetch = [&](int kt) {
-        const int r = wave * 64 + lane;
         const int kb = kt * KT_BYTES;
-        if (wave * 64 < BM) {
-            const uint32_t v = (kb < g.kbytes) ? (uint32_t)(r * g.ldx + kb) : OOB_OFFSET;
+        uint32_t v = OOB_OFFSET;
+        if (wave == 0) {
+            constexpr int RX = BM / PF_SHARE_X;
+            if (lane < RX && kb < g.kbytes) v = (uint32_t)(((tn % PF_SHARE_X) * RX + lane) * g.ldx + kb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
         } else {
-            const int rr = r - BM;
-            const uint32_t v = (rr < BN && kb < g.kbytes) ? (uint32_t)(rr * g.ldw + kb) : OOB_OFFSET;
+            const int rw_rows = BN / g.group_m;
+            if (wave == 1 && lane < rw_rows && kb < g.kbytes)
+                v = (uint32_t)(((tm % g.group_m) * rw_rows + lane) * g.ldw + kb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)sink, 4, v, 0, 0, 0);
         }
     };
@@ -228,7 +241,6 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
     int pm0 = 0, pn0 = 0;
     bool have_prev = false;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        int tm, tn;
         tile_of_block(t, nt_m, nt_n, g.group_m, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
         rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
