@@ -215,10 +215,61 @@ rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx,
                                int8_t *xq, int64_t ldq, float *x_scale,
                                int64_t m, int64_t k, void *stream);
 
+/*
+ * rpl_matmul_reduce_rmsnorm -- the whole path for a decode-sized block of token
+ * rows in one launch: every shard's product, their sum, residual add, RMSNorm.
+ *
+ * [910C] communication-fusion section: one operator holds o_proj matmul +
+ * AllReduce + residual add + RMSNorm for up to 40 rows (a decode step with
+ * speculative tokens); its fallback is matmul + all_reduce + add_rms_norm.  On
+ * one GPU all tp shards' products for the rows are computed in the same launch:
+ *   P_s[i, j]    = bf16_rne( sum_k x_shards[s][i, k] * w_shards[s][j, k] )
+ *                  (rows m_valid <= i < m are padding: P_s = 0)
+ *   h[i, j]      = sum_s P_s[i, j] + residual[i, j]                (fp32)
+ *   residual_out = bf16_rne(h);  y = bf16_rne(gamma * h / sqrt(mean_j h^2 + eps))
+ * Each shard's product is rounded to bf16 before the sum, as a partial crossing
+ * the wire would be, so the result equals rpl_partial per shard followed by
+ * rpl_reduce_chunk_rmsnorm on these rows (within the bf16 rule: fp32 sums).
+ * With the rows of one reduce-scatter chunk this is rank c's step; with all M
+ * rows it is the all-reduce form of [MMAR] plus the epilogue.
+ *
+ * x_shards   HOST array of tp DEVICE pointers, each -> [m_valid, k] bf16 (shard
+ *            s's activation rows of the block), row stride ldx >= k
+ * w_shards   HOST array of tp DEVICE pointers, each -> [n, k] bf16, stride ldw >= k
+ * residual   [m, n] bf16 contiguous; residual_out [m, n] bf16 (may be exactly
+ *            residual); y [m, n] bf16; gamma [n] bf16; eps >= 0, finite
+ * workspace  device buffer of at least rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
+ *            bytes, 256-byte aligned.  Its first 4 bytes must be zero before its
+ *            first use; every call leaves them zero again.  Calls that share a
+ *            workspace must not run concurrently (same stream is fine).
+ * y, residual_out and workspace must not overlap inputs or each other (except
+ * residual_out == residual).
+ *
+ * RPL_ERR_NULL        m > 0 and a pointer (or an entry x_shards[s], w_shards[s],
+ *                     s < tp <= RPL_MAX_TP) is NULL
+ * RPL_ERR_INVALID     m < 0, m_valid < 0 or > m, n < 1, k < 1, tp < 1, ldx < k,
+ *                     ldw < k, eps < 0 or not finite, workspace too small,
+ *                     overlaps
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; m > 64; n, k, ldx or ldw not a multiple
+ *                     of 8; bf16 pointers not 16-byte aligned, workspace not
+ *                     256-byte aligned; n or k >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n);
+
+rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx,
+                                     const rpl_bf16 *const *w_shards, int64_t ldw,
+                                     int32_t tp, int64_t m, int64_t m_valid,
+                                     int64_t n, int64_t k,
+                                     const rpl_bf16 *residual, const rpl_bf16 *gamma,
+                                     float eps, rpl_bf16 *y, rpl_bf16 *residual_out,
+                                     void *workspace, int64_t workspace_bytes,
+                                     void *stream);
+
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 1.1. */
+/* Library ABI version: (major << 16) | minor.  Currently 1.2. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

@@ -13,6 +13,8 @@ the library is missing, every call raises.
     rpl_w8a8_partial(xq, x_scale, wq, w_scale, tp, want_acc=False)
                                                -> out (, acc)
     rpl_quant_per_token(x)                     -> (xq int8, x_scale fp32)
+    rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps)
+                                               -> (y, residual_out), one launch
 """
 from __future__ import annotations
 
@@ -50,6 +52,11 @@ def lib() -> ctypes.CDLL:
         L.rpl_reduce_chunk_rmsnorm.argtypes = [_p, _i32, _i64, _i64, _p, _p, ctypes.c_float, _p, _p, _p]
         L.rpl_w8a8_partial.restype = ctypes.c_int
         L.rpl_w8a8_partial.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
+        L.rpl_matmul_reduce_rmsnorm_workspace_size.restype = _i64
+        L.rpl_matmul_reduce_rmsnorm_workspace_size.argtypes = [_i64, _i64]
+        L.rpl_matmul_reduce_rmsnorm.restype = ctypes.c_int
+        L.rpl_matmul_reduce_rmsnorm.argtypes = [_p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _p,
+                                                ctypes.c_float, _p, _p, _p, _i64, _p]
         L.rpl_quant_per_token.restype = ctypes.c_int
         L.rpl_quant_per_token.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
@@ -219,6 +226,60 @@ def rpl_quant_per_token(x, xq=None, x_scale=None, stream=None):
     return xq, x_scale
 
 
+def rpl_matmul_reduce_rmsnorm_workspace(m: int, n: int, device=None):
+    """A zero-filled workspace for rpl_matmul_reduce_rmsnorm on [m, n] (reusable across calls)."""
+    torch = _torch()
+    size = lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
+    if size < 0:
+        raise ValueError(f"unsupported shape m={m} n={n} for rpl_matmul_reduce_rmsnorm")
+    return torch.zeros(max(size, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps: float, workspace=None, y=None,
+                              residual_out=None, stream=None):
+    """Single launch: every shard's product for the rows, their sum, residual add, RMSNorm.
+
+    x_shards: tp tensors [m_valid, k] (the block's activation rows per shard, same row stride);
+    w_shards: tp tensors [n, k]; residual [m, n]; gamma [n].  Rows m_valid..m-1 are padding.
+    Returns (y, residual_out).
+    """
+    torch = _torch()
+    tp = len(w_shards)
+    if tp < 1 or len(x_shards) != tp:
+        raise ValueError("need as many activation shards as weight shards (at least one)")
+    _dev(residual, "residual", torch.bfloat16, 2)
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    m, n = residual.shape
+    for i, t in enumerate(w_shards):
+        _dev(t, f"w_shards[{i}]", torch.bfloat16, 2)
+    for i, t in enumerate(x_shards):
+        _dev(t, f"x_shards[{i}]", torch.bfloat16, 2)
+    k = w_shards[0].shape[1]
+    m_valid = x_shards[0].shape[0]
+    if any(t.shape != (n, k) for t in w_shards) or any(t.shape != (m_valid, k) for t in x_shards):
+        raise ValueError("shard shapes disagree")
+    ldx, ldw = _ld(x_shards[0]), _ld(w_shards[0])
+    if any(_ld(t) != ldx for t in x_shards) or any(_ld(t) != ldw for t in w_shards):
+        raise ValueError("all shards must share one row stride")
+    if not residual.is_contiguous():
+        raise ValueError("residual must be contiguous")
+    if y is None:
+        y = torch.empty_like(residual)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    if workspace is None:
+        workspace = rpl_matmul_reduce_rmsnorm_workspace(m, n, residual.device)
+    xs = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in x_shards])
+    ws = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in w_shards])
+    st = lib().rpl_matmul_reduce_rmsnorm(ctypes.cast(xs, _p), ldx, ctypes.cast(ws, _p), ldw, tp, m, m_valid, n, k,
+                                         residual.data_ptr(), gamma.data_ptr(), float(eps), y.data_ptr(),
+                                         residual_out.data_ptr(), workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), _stream(residual, stream))
+    _check("rpl_matmul_reduce_rmsnorm", st)
+    return y, residual_out
+
+
 __all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
+           "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace",
            "rpl_status_string", "rpl_version",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

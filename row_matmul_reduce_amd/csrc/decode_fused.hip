@@ -1,0 +1,193 @@
+// decode_fused.hip -- the whole path for a decode-sized block of token rows in
+// one launch on gfx950: every tensor-parallel shard's product, the sum of the
+// shards, residual add and RMSNorm.
+//
+// What it computes (Dewu tech blog "国产算力·昇腾 910C 大模型推理优化（下）：源码修改与
+// 算子优化", communication-fusion section: one operator holds o_proj matmul +
+// AllReduce + residual add + RMSNorm for up to 40 rows, reducing across ranks as
+// matmul tiles finish and normalising with a cross-rank sum of squares; its
+// fallback is the unfused composition matmul + all_reduce + add_rms_norm):
+//   P_s[i, j]       = bf16( sum_k x_s[i, k] * w_s[j, k] )     (pad rows i >= m_valid: 0)
+//   h[i, j]         = sum_s P_s[i, j] + residual[i, j]         (fp32)
+//   residual_out    = bf16(h)
+//   y[i, j]         = bf16( gamma[j] * h[i, j] * rsqrt(mean_j h[i, :]^2 + eps) )
+// Each shard's product is rounded to bf16 before the sum, exactly as a partial
+// crosses the wire in the unfused path, so both paths have one definition.
+//
+// One workgroup per 16 output columns, 4 waves splitting K (as the decode
+// partial).  Per shard: each wave's MFMA partial meets the others in LDS, wave 0
+// rounds the shard's product to bf16 and adds it to its running fp32 sum.  After
+// the residual add, wave 0 writes residual_out, the fp32 h of its columns and
+// each row's partial sum of squares over its 16 columns to the workspace.  The
+// row norm needs every column: the workgroup that finishes last (a device-scope
+// counter in the workspace, incremented once per workgroup after a release
+// fence) sums the partial sums, then writes y for all columns from the fp32 h,
+// and resets the counter.  No workgroup waits for another, so nothing spins.
+#include "rpl_device.h"
+#include "rpl_launch.h"
+
+namespace rpl {
+
+constexpr int FD_WAVES = 4;
+constexpr int FD_BATCH = 8;  // K steps (32 values each) whose loads are issued together
+
+template <int RB>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * FD_WAVES, 64 * FD_WAVES)))
+decode_fused_kernel(FusedDecodeArgs a) {
+    __shared__ f32x4 red[FD_WAVES - 1][RB][64];
+    __shared__ float inv_rms[16 * RB];
+    __shared__ int last_flag;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nblk = gridDim.x;
+    const int n0 = blockIdx.x * 16;
+    const int steps = (a.k + 31) / 32;
+    const int per = (steps + FD_WAVES - 1) / FD_WAVES;
+    const int s_begin = wave * per, s_end = min(steps, s_begin + per);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int wrow = n0 + r16;
+    const bool wrow_ok = wrow < a.n;
+
+    f32x4 hsum[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) hsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < a.tp; ++s) {
+        const uint16_t *wp = a.w[s] + (int64_t)(wrow_ok ? wrow : 0) * a.ldw + g * 8;
+        f32x4 acc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t0 = s_begin; t0 < s_end; t0 += FD_BATCH) {
+            u32x4 wf[FD_BATCH], xf[FD_BATCH][RB];
+#pragma unroll
+            for (int j = 0; j < FD_BATCH; ++j) {
+                const int t = t0 + j;
+                const int kel = t * 32 + g * 8;
+                const bool live = t < s_end && kel < a.k;
+                wf[j] = (live && wrow_ok) ? ld16(wp + t * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int xrow = rb * 16 + r16;
+                    xf[j][rb] = (live && xrow < a.m_valid) ? ld16(a.x[s] + (int64_t)xrow * a.ldx + kel)
+                                                           : u32x4{0, 0, 0, 0};
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < FD_BATCH; ++j)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j]),
+                                                                      __builtin_bit_cast(bf16x8, xf[j][rb]),
+                                                                      acc[rb], 0, 0, 0);
+        }
+        if (wave > 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) red[wave - 1][rb][lane] = acc[rb];
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                f32x4 p = acc[rb];
+#pragma unroll
+                for (int v = 0; v < FD_WAVES - 1; ++v) p += red[v][rb][lane];
+                // the shard's product as it would cross the wire: bf16, nearest-even
+                const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
+                hsum[rb] += f32x4{bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi)};
+            }
+        }
+        __syncthreads();  // red is reused by the next shard
+    }
+
+    // Lane (wave 0) holds h for token row rb*16 + r16, columns n0 + 4g .. n0 + 4g + 3.
+    if (wave == 0) {
+        const int col = n0 + g * 4;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = rb * 16 + r16;
+            float ss = 0.f;
+            if (row < a.m && col < a.n) {
+                const int64_t off = (int64_t)row * a.n + col;
+                const u32x2 rv = *reinterpret_cast<const u32x2 *>(a.residual + off);
+                const f32x4 h = hsum[rb] + f32x4{bf16_lo(rv[0]), bf16_hi(rv[0]), bf16_lo(rv[1]), bf16_hi(rv[1])};
+                st8(a.residual_out + off, u32x2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])});
+                *reinterpret_cast<f32x4 *>(a.h_ws + off) = h;
+                ss = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
+            }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (g == 0 && row < a.m) a.ss_ws[(int64_t)row * nblk + blockIdx.x] = ss;
+        }
+    }
+    __threadfence();  // release this workgroup's h and partial sums at device scope
+    __syncthreads();
+    if (threadIdx.x == 0) last_flag = (atomicAdd(a.counter, 1u) == (unsigned)nblk - 1) ? 1 : 0;
+    __syncthreads();
+    if (!last_flag) return;
+
+    // Last workgroup: every other workgroup's results are visible after an acquire fence.
+    __threadfence();
+    for (int row = wave; row < a.m; row += FD_WAVES) {
+        float ss = 0.f;
+        for (int b = lane; b < nblk; b += 64) ss += a.ss_ws[(int64_t)row * nblk + b];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (lane == 0) inv_rms[row] = rsqrtf(ss / (float)a.n + a.eps);
+    }
+    __syncthreads();
+    const int nch = a.n / 8;  // 8 outputs per chunk
+    const int total = a.m * nch;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * 4) {
+        f32x4 hv[4][2];
+        u32x4 gv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * 256;
+            if (c < total) {
+                const int row = c / nch, cc = c - row * nch;
+                const float *hp = a.h_ws + (int64_t)row * a.n + cc * 8;
+                hv[u][0] = *reinterpret_cast<const f32x4 *>(hp);
+                hv[u][1] = *reinterpret_cast<const f32x4 *>(hp + 4);
+                gv[u] = ld16(a.gamma + cc * 8);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * 256;
+            if (c < total) {
+                const int row = c / nch, cc = c - row * nch;
+                const float inv = inv_rms[row];
+                u32x4 yo;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float h0 = hv[u][q >> 1][(q & 1) * 2], h1 = hv[u][q >> 1][(q & 1) * 2 + 1];
+                    yo[q] = pack_bf16x2(bf16_lo(gv[u][q]) * (h0 * inv), bf16_hi(gv[u][q]) * (h1 * inv));
+                }
+                st16(a.y + (int64_t)row * a.n + cc * 8, yo);
+            }
+        }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+int64_t fused_decode_ss_bytes(int64_t m, int64_t n) {
+    const int64_t nblk = (n + 15) / 16;
+    return (4 * m * nblk + 255) / 256 * 256;
+}
+
+int64_t fused_decode_workspace_bytes(int64_t m, int64_t n) {
+    return FD_WS_HEADER + fused_decode_ss_bytes(m, n) + 4 * m * n;
+}
+
+hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st) {
+    const dim3 grid((a.n + 15) / 16), block(64 * FD_WAVES);
+    switch ((a.m + 15) / 16) {
+        case 1: hipLaunchKernelGGL(decode_fused_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(decode_fused_kernel<2>, grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL(decode_fused_kernel<3>, grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL(decode_fused_kernel<4>, grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace rpl

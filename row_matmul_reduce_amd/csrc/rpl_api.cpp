@@ -146,6 +146,77 @@ rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx, int8_t *xq, int64
                                                      static_cast<hipStream_t>(stream)));
 }
 
+int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n) {
+    if (m < 0 || n < 1 || m > 64 || n > kMaxDim) return -1;
+    return rpl::fused_decode_workspace_bytes(m, n);
+}
+
+rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx, const rpl_bf16 *const *w_shards,
+                                     int64_t ldw, int32_t tp, int64_t m, int64_t m_valid, int64_t n, int64_t k,
+                                     const rpl_bf16 *residual, const rpl_bf16 *gamma, float eps, rpl_bf16 *y,
+                                     rpl_bf16 *residual_out, void *workspace, int64_t workspace_bytes,
+                                     void *stream) {
+    if (!x_shards || !w_shards || !gamma) return RPL_ERR_NULL;
+    if (m != 0) {
+        if (!residual || !y || !residual_out || !workspace) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!w_shards[s] || (m_valid > 0 && !x_shards[s])) return RPL_ERR_NULL;
+    }
+    if (m < 0 || m_valid < 0 || m_valid > m || n < 1 || k < 1 || tp < 1 || ldx < k || ldw < k ||
+        !(eps >= 0.0f) || !std::isfinite(eps))
+        return RPL_ERR_INVALID;
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    const int64_t mat = span(m, n, n, 2), gb = span(1, n, n, 2);
+    const int64_t xb = span(m_valid, k, ldx, 2), wb = span(n, k, ldw, 2);
+    const int64_t need = (m <= 64 && n <= kMaxDim) ? rpl::fused_decode_workspace_bytes(m, n) : 0;
+    if (m != 0 && workspace_bytes < need) return RPL_ERR_INVALID;
+    const int64_t wsb = workspace_bytes < 0 ? 0 : workspace_bytes;
+    // outputs and workspace against the inputs and each other
+    const void *outs[3] = {y, residual_out, workspace};
+    const int64_t osz[3] = {mat, mat, wsb};
+    for (int o = 0; o < 3; ++o) {
+        if (o != 1 || residual_out != residual)
+            if (overlap(outs[o], osz[o], residual, mat)) return RPL_ERR_INVALID;
+        if (overlap(outs[o], osz[o], gamma, gb)) return RPL_ERR_INVALID;
+        for (int s = 0; s < np; ++s)
+            if (overlap(outs[o], osz[o], x_shards[s], xb) || overlap(outs[o], osz[o], w_shards[s], wb))
+                return RPL_ERR_INVALID;
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], osz[o], outs[q], osz[q])) return RPL_ERR_INVALID;
+    }
+    if (tp > RPL_MAX_TP || m > 64 || n % 8 || k % 8 || ldx % 8 || ldw % 8) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(y, 16) || !aligned(residual_out, 16) ||
+        !aligned(workspace, 256))
+        return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp; ++s)
+        if (!aligned(w_shards[s], 16) || !aligned(x_shards[s], 16)) return RPL_ERR_UNSUPPORTED;
+    if (n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    rpl::FusedDecodeArgs a{};
+    for (int s = 0; s < tp; ++s) {
+        a.x[s] = x_shards[s];
+        a.w[s] = w_shards[s];
+    }
+    a.ldx = ldx;
+    a.ldw = ldw;
+    a.tp = tp;
+    a.m = (int)m;
+    a.m_valid = (int)m_valid;
+    a.n = (int)n;
+    a.k = (int)k;
+    a.residual = residual;
+    a.gamma = gamma;
+    a.eps = eps;
+    a.y = y;
+    a.residual_out = residual_out;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    a.counter = reinterpret_cast<unsigned *>(ws);
+    a.ss_ws = reinterpret_cast<float *>(ws + rpl::FD_WS_HEADER);
+    a.h_ws = reinterpret_cast<float *>(ws + rpl::FD_WS_HEADER + rpl::fused_decode_ss_bytes(m, n));
+    return launch_status(rpl::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
+}
+
 const char *rpl_status_string(rpl_status s) {
     switch (s) {
         case RPL_OK: return "RPL_OK";
@@ -157,6 +228,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (1 << 16) | 1; }
+int32_t rpl_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

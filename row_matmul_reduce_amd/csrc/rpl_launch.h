@@ -24,6 +24,25 @@ hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int 
                                  const uint16_t *gamma, float eps, uint16_t *y, uint16_t *residual_out,
                                  hipStream_t st);
 
+// The single-launch decode path (decode_fused.hip).  Workspace layout: a 256-byte
+// header whose first word is the completion counter, then the per-row partial sums of
+// squares [m][nblk] fp32 (padded to 256 bytes), then h [m][n] fp32.
+constexpr int64_t FD_WS_HEADER = 256;
+struct FusedDecodeArgs {
+    const uint16_t *x[MAX_TP];  // per shard: [m_valid, k] rows, stride ldx
+    const uint16_t *w[MAX_TP];  // per shard: [n, k], stride ldw
+    int64_t ldx, ldw;
+    int tp, m, m_valid, n, k;
+    const uint16_t *residual, *gamma;
+    float eps;
+    uint16_t *y, *residual_out;
+    float *ss_ws, *h_ws;
+    unsigned *counter;
+};
+int64_t fused_decode_workspace_bytes(int64_t m, int64_t n);
+int64_t fused_decode_ss_bytes(int64_t m, int64_t n);
+hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st);
+
 hipError_t launch_quant_per_token(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq, float *scale, int m,
                                   int k, hipStream_t st);
 

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_path_calls():
     names = declared_functions()
     for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
+              "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace_size",
               "rpl_status_string", "rpl_version"):
         assert f in names
 
@@ -50,7 +51,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (1 << 16) | 1
+    assert rpl.rpl_version() == (1 << 16) | 2
 
 
 class Buf:
@@ -225,6 +226,62 @@ def test_quant_validation():
     for b in (X, Q, S):
         assert b.untouched()
     assert quant_call(None, k, None, k, None, 0, k) == OK
+
+
+def fused_call(xs, ldx, ws, ldw, tp, m, mv, n, k, res, gam, eps, y, ro, work, wbytes):
+    import ctypes
+    xa = (ctypes.c_void_p * max(tp, 1))(*(xs + [None] * max(0, tp - len(xs)))[:max(tp, 1)])
+    wa = (ctypes.c_void_p * max(tp, 1))(*(ws + [None] * max(0, tp - len(ws)))[:max(tp, 1)])
+    return rpl.lib().rpl_matmul_reduce_rmsnorm(ctypes.cast(xa, ctypes.c_void_p), ldx, ctypes.cast(wa, ctypes.c_void_p),
+                                               ldw, tp, m, mv, n, k, res, gam, eps, y, ro, work, wbytes, None)
+
+
+def test_fused_decode_workspace_size():
+    L = rpl.lib()
+    # header 256 B + per-row partial sums [m][n/16] fp32 padded to 256 B + h [m][n] fp32
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 3584) == 256 + 3584 + 4 * 4 * 3584
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(1, 8) == 256 + 256 + 32
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(65, 64) == -1
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(-1, 64) == -1
+
+
+def test_fused_decode_validation():
+    tp, m, n, k = 2, 4, 64, 32
+    wsz = rpl.lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
+    X0, X1, W0, W1 = Buf(m * k * 2), Buf(m * k * 2), Buf(n * k * 2), Buf(n * k * 2)
+    R, G, Y, RO = Buf(m * n * 2), Buf(n * 2), Buf(m * n * 2), Buf(m * n * 2)
+    WS = Buf(wsz + 512)
+    ws_ptr = WS.ptr + ((-WS.ptr) % 256)
+    xs, wl = [X0.ptr, X1.ptr], [W0.ptr, W1.ptr]
+    r, g, y, ro = R.ptr, G.ptr, Y.ptr, RO.ptr
+    base = (xs, k, wl, k, tp, m, m, n, k, r, g, 1e-6, y, ro, ws_ptr, wsz)
+
+    def case(**kw):
+        names = ["xs", "ldx", "ws", "ldw", "tp", "m", "mv", "n", "k", "res", "gam", "eps", "y", "ro", "work", "wbytes"]
+        a = dict(zip(names, base))
+        a.update(kw)
+        return fused_call(*[a[nm] for nm in names])
+
+    cases = [
+        (dict(xs=[X0.ptr, None]), NULL), (dict(ws=[None, W1.ptr]), NULL), (dict(res=None), NULL),
+        (dict(gam=None), NULL), (dict(y=None), NULL), (dict(work=None), NULL),
+        (dict(m=-1), INVALID), (dict(mv=5), INVALID), (dict(mv=-1), INVALID), (dict(n=0), INVALID),
+        (dict(k=0), INVALID), (dict(tp=0), INVALID), (dict(ldx=24), INVALID), (dict(ldw=24), INVALID),
+        (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(wbytes=wsz - 1), INVALID),
+        (dict(y=r), INVALID),                       # y aliases the residual
+        (dict(ro=y), INVALID),                      # residual_out aliases y
+        (dict(work=ws_ptr, y=ws_ptr + 256), INVALID),  # y inside the workspace
+        (dict(ro=r + 16), INVALID),                 # residual_out partially overlaps the residual
+        (dict(tp=17, xs=xs * 9, ws=wl * 9), UNSUP), (dict(m=65, mv=4, res=1 << 40, y=1 << 41, ro=1 << 42, work=1 << 43, wbytes=1 << 20), UNSUP),
+        (dict(n=60, res=1 << 40, y=1 << 41, ro=1 << 42, work=1 << 43, wbytes=1 << 20), UNSUP), (dict(k=36, ldx=40, ldw=40), UNSUP), (dict(ldx=36), UNSUP),
+        (dict(xs=[X0.ptr + 8, X1.ptr]), UNSUP), (dict(work=ws_ptr + 16, wbytes=wsz), UNSUP),
+        (dict(y=y + 8), UNSUP),
+    ]
+    for kw, want in cases:
+        assert case(**kw) == want, kw
+    for b in (X0, X1, W0, W1, R, G, Y, RO, WS):
+        assert b.untouched()
+    assert case(m=0, mv=0, res=None, y=None, ro=None, work=None, wbytes=0) == OK
 
 
 def test_binding_rejects_host_tensors():
