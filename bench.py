@@ -17,7 +17,9 @@ partial consumes.  A model layer runs the bf16 or the w8a8 partial, not both,
 so each precision is its own path.  The default run times the bf16 prefill down_proj share
 (M=4096, K_full=18944 over TP=2, N=3584) as the main step, and in the same run
 the w8a8 twin, the decode o_proj share and the TP=8 long-prefill share as side
-steps (w8a8 both from int8 inputs and from the bf16 activation).  Every step cycles through several copies of its inputs (more than
+steps (w8a8 both from int8 inputs and from the bf16 activation), plus the
+single-launch decode path (every shard's product + sum + residual + RMSNorm in one
+kernel) for a token chunk and for all rows.  Every step cycles through several copies of its inputs (more than
 twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
@@ -49,6 +51,7 @@ KERNEL_SOURCES = {
     "partial_w8a8": ["gemm_nt.h", "gemm_w8a8.hip", "rpl_device.h"],
     "reduce_rmsnorm": ["reduce_rmsnorm.hip", "rpl_device.h"],
     "quant_per_token": ["quant_per_token.hip", "rpl_device.h"],
+    "decode_fused": ["decode_fused.hip", "rpl_device.h"],
 }
 WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
@@ -241,6 +244,50 @@ class Path:
         return rep
 
 
+def fused_decode(torch, rpl, copies: int, all_rows: bool, launches: int = 200):
+    """The single-launch decode path (every shard's product + sum + residual + RMSNorm) on the
+    decode o_proj workload: rank 0's token chunk (reduce-scatter form) or all rows (all-reduce
+    form).  Timed by replaying a HIP graph of `launches` launches over rotated weight copies."""
+    from row_matmul_reduce_amd import synth
+    wl = synth.WORKLOADS[WORKLOAD_IDS["decode"]]
+    rows = wl.m if all_rows else wl.m_chunk
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    xs = [bf(synth.x_shard(wl, s, rows=rows)) for s in range(wl.tp)]
+    ws = [bf(synth.w_shard(wl, s)) for s in range(wl.tp)]
+    res = bf(np.tile(synth.residual_chunk(wl), (-(-rows // wl.m_chunk), 1))[:rows])
+    gam = bf(synth.gamma(wl))
+    set_bytes = sum(t.numel() * 2 for t in ws)
+    if copies <= 0:
+        copies = max(3, -(-(2 * MALL_BYTES + 1) // set_bytes) + 1)
+    sets = [ws] + [[t.clone() for t in ws] for _ in range(copies - 1)]
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(rows, wl.n)
+    y = torch.empty_like(res)
+    ro = torch.empty_like(res)
+    for i in range(len(sets)):
+        rpl.rpl_matmul_reduce_rmsnorm(xs, sets[i], res, gam, wl.eps, workspace=work, y=y, residual_out=ro)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            rpl.rpl_matmul_reduce_rmsnorm(xs, sets[i % len(sets)], res, gam, wl.eps, workspace=work, y=y,
+                                          residual_out=ro)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / launches
+    nbytes = (wl.tp * wl.n * wl.k_shard * 2 + wl.tp * rows * wl.k_shard * 2 + 3 * rows * wl.n * 2 + wl.n * 2)
+    return {"workload": wl.name, "rows": rows, "form": "all-reduce" if all_rows else "reduce-scatter chunk",
+            "shards": wl.tp, "us": us, "bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "weight_sets_rotated": len(sets)}
+
+
 def library_reference(path, torch, steps: int):
     """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
     HBM-resident input sets, same stream and timing method, to show what the chip gives under the
@@ -367,6 +414,11 @@ def main():
             side[key] = {"workload": swl.name, "ms_per_step": s_ms, "input_sets_rotated": len(sp.sets),
                          "kernels": sp.kernels_report(s_kern, s_period)}
             del sp
+            torch.cuda.empty_cache()
+
+    if not args.no_side and args.workload == "prefill":
+        for key, all_rows in (("decode_fused_chunk", False), ("decode_fused_allreduce", True)):
+            side[key] = fused_decode(torch, rpl, args.copies, all_rows)
             torch.cuda.empty_cache()
 
     cpu = None

@@ -14,9 +14,12 @@
 // Each shard's product is rounded to bf16 before the sum, exactly as a partial
 // crosses the wire in the unfused path, so both paths have one definition.
 //
-// One workgroup per 16 output columns, 4 waves splitting K (as the decode
-// partial).  Per shard: each wave's MFMA partial meets the others in LDS, wave 0
-// rounds the shard's product to bf16 and adds it to its running fp32 sum.  After
+// One workgroup per 16 output columns, 8 waves: the shards' products are computed
+// concurrently by groups of 8/tp waves (up to 8 shards per pass), each group
+// splitting its shard's K range; every wave issues up to 16 K steps of loads
+// before its MFMAs.  The waves' MFMA partials meet in LDS, where wave 0 sums each
+// shard's group, rounds the shard's product to bf16 and adds it to a running fp32
+// sum.  After
 // the residual add, wave 0 writes residual_out, the fp32 h of its columns and
 // each row's partial sum of squares over its 16 columns to the workspace.  The
 // row norm needs every column: the workgroup that finishes last (a device-scope
@@ -28,74 +31,85 @@
 
 namespace rpl {
 
-constexpr int FD_WAVES = 4;
-constexpr int FD_BATCH = 8;  // K steps (32 values each) whose loads are issued together
+constexpr int FD_WAVES = 8;
+
+// Waves per shard: the 8 waves split into tp groups (up to 8 shards at once); a group
+// splits its shard's K range.  More than 8 shards are taken 8 at a time.
+__device__ __forceinline__ int fd_waves_per_shard(int tp) { return tp >= FD_WAVES ? 1 : FD_WAVES / tp; }
 
 template <int RB>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * FD_WAVES, 64 * FD_WAVES)))
 decode_fused_kernel(FusedDecodeArgs a) {
-    __shared__ f32x4 red[FD_WAVES - 1][RB][64];
+    constexpr int BATCH = RB <= 2 ? 16 : 8;  // K steps (32 values each) whose loads are issued together
+    __shared__ f32x4 red[FD_WAVES][RB][64];
     __shared__ float inv_rms[16 * RB];
     __shared__ int last_flag;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nblk = gridDim.x;
     const int n0 = blockIdx.x * 16;
     const int steps = (a.k + 31) / 32;
-    const int per = (steps + FD_WAVES - 1) / FD_WAVES;
-    const int s_begin = wave * per, s_end = min(steps, s_begin + per);
+    const int wps = fd_waves_per_shard(a.tp);
+    const int group = wave / wps, sub = wave % wps;         // shard group, position in it
+    const int per = (steps + wps - 1) / wps;
+    const int s_begin = sub * per, s_end = min(steps, s_begin + per);
     const int r16 = lane & 15, g = lane >> 4;
     const int wrow = n0 + r16;
     const bool wrow_ok = wrow < a.n;
+    const int groups = FD_WAVES / wps;                       // shards handled per pass
 
     f32x4 hsum[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) hsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = 0; s < a.tp; ++s) {
-        const uint16_t *wp = a.w[s] + (int64_t)(wrow_ok ? wrow : 0) * a.ldw + g * 8;
+    for (int s0 = 0; s0 < a.tp; s0 += groups) {
+        const int s = s0 + group;
+        const bool shard_ok = group < groups && s < a.tp;
         f32x4 acc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int t0 = s_begin; t0 < s_end; t0 += FD_BATCH) {
-            u32x4 wf[FD_BATCH], xf[FD_BATCH][RB];
+        if (shard_ok) {
+            const uint16_t *wp = a.w[s] + (int64_t)(wrow_ok ? wrow : 0) * a.ldw + g * 8;
+            for (int t0 = s_begin; t0 < s_end; t0 += BATCH) {
+                u32x4 wf[BATCH], xf[BATCH][RB];
 #pragma unroll
-            for (int j = 0; j < FD_BATCH; ++j) {
-                const int t = t0 + j;
-                const int kel = t * 32 + g * 8;
-                const bool live = t < s_end && kel < a.k;
-                wf[j] = (live && wrow_ok) ? ld16(wp + t * 32) : u32x4{0, 0, 0, 0};
+                for (int j = 0; j < BATCH; ++j) {
+                    const int t = t0 + j;
+                    const int kel = t * 32 + g * 8;
+                    const bool live = t < s_end && kel < a.k;
+                    wf[j] = (live && wrow_ok) ? ld16(wp + t * 32) : u32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const int xrow = rb * 16 + r16;
-                    xf[j][rb] = (live && xrow < a.m_valid) ? ld16(a.x[s] + (int64_t)xrow * a.ldx + kel)
-                                                           : u32x4{0, 0, 0, 0};
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const int xrow = rb * 16 + r16;
+                        xf[j][rb] = (live && xrow < a.m_valid) ? ld16(a.x[s] + (int64_t)xrow * a.ldx + kel)
+                                                               : u32x4{0, 0, 0, 0};
+                    }
                 }
+#pragma unroll
+                for (int j = 0; j < BATCH; ++j)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j]),
+                                                                          __builtin_bit_cast(bf16x8, xf[j][rb]),
+                                                                          acc[rb], 0, 0, 0);
             }
-#pragma unroll
-            for (int j = 0; j < FD_BATCH; ++j)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j]),
-                                                                      __builtin_bit_cast(bf16x8, xf[j][rb]),
-                                                                      acc[rb], 0, 0, 0);
         }
-        if (wave > 0) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) red[wave - 1][rb][lane] = acc[rb];
-        }
+        for (int rb = 0; rb < RB; ++rb) red[wave][rb][lane] = acc[rb];
         __syncthreads();
         if (wave == 0) {
+            // shards in order: each shard's waves summed in order, rounded to bf16 (the
+            // product as it would cross the wire), added to the running fp32 sum
+            for (int q = 0; q < groups && s0 + q < a.tp; ++q) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                f32x4 p = acc[rb];
-#pragma unroll
-                for (int v = 0; v < FD_WAVES - 1; ++v) p += red[v][rb][lane];
-                // the shard's product as it would cross the wire: bf16, nearest-even
-                const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
-                hsum[rb] += f32x4{bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi)};
+                for (int rb = 0; rb < RB; ++rb) {
+                    f32x4 p = red[q * wps][rb][lane];
+                    for (int v = 1; v < wps; ++v) p += red[q * wps + v][rb][lane];
+                    const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
+                    hsum[rb] += f32x4{bf16_lo(lo), bf16_hi(lo), bf16_lo(hi), bf16_hi(hi)};
+                }
             }
         }
-        __syncthreads();  // red is reused by the next shard
+        __syncthreads();  // red is reused by the next pass
     }
 
     // Lane (wave 0) holds h for token row rb*16 + r16, columns n0 + 4g .. n0 + 4g + 3.
@@ -117,31 +131,27 @@ decode_fused_kernel(FusedDecodeArgs a) {
             ss += __shfl_xor(ss, 32, 64);
             if (g == 0 && row < a.m) a.ss_ws[(int64_t)row * nblk + blockIdx.x] = ss;
         }
+        // Release this workgroup's h and partial sums at device scope (an L2 write-back on
+        // this multi-XCD part, so only the one wave that wrote them pays it), then count in.
+        __threadfence();
+        if (lane == 0) last_flag = (atomicAdd(a.counter, 1u) == (unsigned)nblk - 1) ? 1 : 0;
     }
-    __threadfence();  // release this workgroup's h and partial sums at device scope
-    __syncthreads();
-    if (threadIdx.x == 0) last_flag = (atomicAdd(a.counter, 1u) == (unsigned)nblk - 1) ? 1 : 0;
     __syncthreads();
     if (!last_flag) return;
 
     // Last workgroup: every other workgroup's results are visible after an acquire fence.
+    // The first batch of h and gamma loads is issued before the partial sums are reduced,
+    // so the two round trips overlap.
     __threadfence();
-    for (int row = wave; row < a.m; row += FD_WAVES) {
-        float ss = 0.f;
-        for (int b = lane; b < nblk; b += 64) ss += a.ss_ws[(int64_t)row * nblk + b];
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if (lane == 0) inv_rms[row] = rsqrtf(ss / (float)a.n + a.eps);
-    }
-    __syncthreads();
+    constexpr int U = 4;
     const int nch = a.n / 8;  // 8 outputs per chunk
     const int total = a.m * nch;
-    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * 4) {
-        f32x4 hv[4][2];
-        u32x4 gv[4];
+    f32x4 hv[U][2];
+    u32x4 gv[U];
+    auto load_batch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = c0 + u * 256;
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 64 * FD_WAVES;
             if (c < total) {
                 const int row = c / nch, cc = c - row * nch;
                 const float *hp = a.h_ws + (int64_t)row * a.n + cc * 8;
@@ -150,9 +160,21 @@ decode_fused_kernel(FusedDecodeArgs a) {
                 gv[u] = ld16(a.gamma + cc * 8);
             }
         }
+    };
+    load_batch(threadIdx.x);
+    for (int row = wave; row < a.m; row += FD_WAVES) {
+        float ss = 0.f;
+        for (int b = lane; b < nblk; b += 64) ss += a.ss_ws[(int64_t)row * nblk + b];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = c0 + u * 256;
+        for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+        if (lane == 0) inv_rms[row] = rsqrtf(ss / (float)a.n + a.eps);
+    }
+    __syncthreads();
+    for (int c0 = threadIdx.x; c0 < total; c0 += 64 * FD_WAVES * U) {
+        if (c0 != (int)threadIdx.x) load_batch(c0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 64 * FD_WAVES;
             if (c < total) {
                 const int row = c / nch, cc = c - row * nch;
                 const float inv = inv_rms[row];

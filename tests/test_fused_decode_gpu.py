@@ -86,15 +86,16 @@ def test_fused_workspace_reuse_and_in_place():
 
 
 def test_fused_equals_unfused_library_path():
-    """Same rows through rpl_partial per shard + rpl_reduce_chunk_rmsnorm: the bf16 partials are
-    identical by construction, so the outputs agree to the bf16 rule (fp32 sums in both)."""
+    """Same rows through rpl_partial per shard + rpl_reduce_chunk_rmsnorm.  Both round each
+    shard's product to bf16 and sum in fp32, but they split K over different numbers of waves,
+    so single bf16 ulps may differ: compared with the bf16 rule."""
     m, n, k, tp = 16, 1024, 512, 4
     xs, ws, res, gam = _inputs(m, m, n, k, tp, seed=9)
     dx, dw = [dev_bf16(x) for x in xs], [dev_bf16(w) for w in ws]
     y, ro = rpl.rpl_matmul_reduce_rmsnorm(dx, dw, dev_bf16(res), dev_bf16(gam), 1e-6)
     parts = [rpl.rpl_partial(x, w, 1) for x, w in zip(dx, dw)]
     y2, ro2 = rpl.rpl_reduce_chunk_rmsnorm(parts, dev_bf16(res), dev_bf16(gam), 1e-6)
-    assert np.array_equal(host_bf16(ro), host_bf16(ro2)), "same bf16 partials and fp32 sum order"
+    assert_bf16_close(host_bf16(ro), host_bf16(ro2), "residual_out vs unfused")
     assert_bf16_close(host_bf16(y), host_bf16(y2), "y vs unfused")
 
 
