@@ -17,6 +17,11 @@ Parity status of each function (what pins it lives in tests/test_oracle_pins.py)
                          scale invariance, zero row, hand-worked golden
   w8a8_rows              pinned: numpy int64 GEMM, sign symmetry, numpy float32
                          dequant in the same operation order
+  sum_partials           pinned: exact rational brute force, permutation invariance
+                         (fp64 sums of bf16 values are exact), integer partials, TP=1
+  reduce_slice_sumsq,    pinned: slices over the whole row reproduce the pinned
+  rmsnorm_slice_apply    reduce_chunk_rmsnorm; exact rational sums of squares;
+                         slice-boundary invariance
   quant_per_token        pinned: exact rational nearest-integer bound, absmax code
                          +-127, power-of-two scale invariance, negation symmetry,
                          zero row, hand-worked ties-to-even golden
@@ -76,6 +81,13 @@ def load(path: str):
                                            ctypes.c_float, _p, _p, _p, _p]
     L.orc_w8a8_rows.restype = ctypes.c_int
     L.orc_w8a8_rows.argtypes = [_p, _i64, _p, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p, _p]
+    L.orc_sum_partials.restype = ctypes.c_int
+    L.orc_sum_partials.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
+    L.orc_reduce_slice_sumsq.restype = ctypes.c_int
+    L.orc_reduce_slice_sumsq.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _p, _p]
+    L.orc_rmsnorm_slice_apply.restype = ctypes.c_int
+    L.orc_rmsnorm_slice_apply.argtypes = [_p, _p, ctypes.c_int, _i64, _i64, _i64, _p, ctypes.c_float, _p,
+                                          _i64, _p]
     L.orc_quant_per_token.restype = ctypes.c_int
     L.orc_quant_per_token.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p]
     L.orc_num_threads.restype = ctypes.c_int
@@ -245,3 +257,63 @@ def quant_per_token(x: np.ndarray, rows: int | None = None):
     if rc != 0:
         raise RuntimeError(f"orc_quant_per_token failed: {rc}")
     return xq, sx
+
+
+def _ptr_array(arrays):
+    arr = (ctypes.c_void_p * len(arrays))(*[a.ctypes.data for a in arrays])
+    return arr
+
+
+def sum_partials(partials, want_f64: bool = False):
+    """bf16(sum of the tp bf16 partials), all rows ([MMAR] all-reduce form)."""
+    parts = [np.ascontiguousarray(p, dtype=np.uint16) for p in partials]
+    m, n = parts[0].shape
+    if any(p.shape != (m, n) for p in parts):
+        raise ValueError("partials disagree in shape")
+    out = np.empty((m, n), dtype=np.uint16)
+    of = np.empty((m, n), dtype=np.float64) if want_f64 else None
+    arr = _ptr_array(parts)
+    rc = lib().orc_sum_partials(ctypes.cast(arr, _p), len(parts), n, m, n, _ptr(out), _ptr(of))
+    if rc != 0:
+        raise RuntimeError(f"orc_sum_partials failed: {rc}")
+    return (out, of) if want_f64 else out
+
+
+def reduce_slice_sumsq(partials, residual, c0: int, n_slice: int):
+    """Step 1 of the hidden-split epilogue for columns [c0, c0 + n_slice) of full [m, n] arrays.
+
+    Returns (residual_out slice uint16 [m, n_slice], h float64 [m, n_slice], sumsq float64 [m]).
+    """
+    parts = [np.ascontiguousarray(p, dtype=np.uint16) for p in partials]
+    residual = np.ascontiguousarray(residual, dtype=np.uint16)
+    m, n = residual.shape
+    if any(p.shape != (m, n) for p in parts) or c0 < 0 or c0 + n_slice > n:
+        raise ValueError("bad slice or shapes")
+    ro = np.zeros((m, n), dtype=np.uint16)
+    h = np.empty((m, n_slice), dtype=np.float64)
+    ss = np.empty((m,), dtype=np.float64)
+    ptrs = (ctypes.c_void_p * len(parts))(*[p.ctypes.data + 2 * c0 for p in parts])
+    rc = lib().orc_reduce_slice_sumsq(ctypes.cast(ptrs, _p), len(parts), n, m, n_slice,
+                                      ctypes.c_void_p(residual.ctypes.data + 2 * c0),
+                                      ctypes.c_void_p(ro.ctypes.data + 2 * c0), _ptr(h), _ptr(ss))
+    if rc != 0:
+        raise RuntimeError(f"orc_reduce_slice_sumsq failed: {rc}")
+    return np.ascontiguousarray(ro[:, c0:c0 + n_slice]), h, ss
+
+
+def rmsnorm_slice_apply(h, sumsq_parts, n_total: int, gamma_slice, eps: float, want_f64: bool = False):
+    """Step 2: y = bf16(gamma * h / sqrt(sum_r sumsq_r / n_total + eps)) for one slice."""
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    m, ns = h.shape
+    parts = [np.ascontiguousarray(s, dtype=np.float64) for s in sumsq_parts]
+    gamma_slice = np.ascontiguousarray(gamma_slice, dtype=np.uint16)
+    if any(p.shape != (m,) for p in parts) or gamma_slice.shape != (ns,):
+        raise ValueError("shape mismatch")
+    y = np.empty((m, ns), dtype=np.uint16)
+    yf = np.empty((m, ns), dtype=np.float64) if want_f64 else None
+    arr = _ptr_array(parts)
+    rc = lib().orc_rmsnorm_slice_apply(_ptr(h), ctypes.cast(arr, _p), len(parts), m, ns, n_total,
+                                       _ptr(gamma_slice), ctypes.c_float(eps), _ptr(y), ns, _ptr(yf))
+    if rc != 0:
+        raise RuntimeError(f"orc_rmsnorm_slice_apply failed: {rc}")
+    return (y, yf) if want_f64 else y

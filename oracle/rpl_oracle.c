@@ -39,7 +39,10 @@
  *       multiplies in that order, then bf16 round-to-nearest-even of the fp32;
  *   R6  per-token dynamic int8 quantisation of the activation: scale = row
  *       absmax / 127 in fp32, code = round-to-nearest-even of x / scale in fp32,
- *       clamped to [-127, 127]; an all-zero row has scale 0 and codes 0.
+ *       clamped to [-127, 127]; an all-zero row has scale 0 and codes 0;
+ *   R7  the 910C layout splits the hidden dimension over ranks: each rank
+ *       reduces a column slice of every row and contributes the slice's sum of
+ *       squares; the full-row sum is their cross-rank sum.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  * OpenMP only splits independent output rows across threads; every dot
@@ -248,6 +251,98 @@ int orc_w8a8_rows(const int8_t *xq, int64_t ldx, const float *sx,
     }
     if (bad) return ORC_ERR_ARG;
     return ovf ? ORC_ERR_OVERFLOW : ORC_OK;
+}
+
+/* ------------------------------------------------- all-reduce form (sum only)
+ * [MMAR] PR description: RowParallelLinear's matmul is fused with its
+ * all-reduce, after which every rank holds the sum of all ranks' partials for
+ * all token rows (no epilogue).  The partials travel as bf16 (R1) and the sum
+ * is delivered as bf16:
+ *   out[i, j] = bf16( sum_s partials[s][i * ldp + j] )      (fp64 sum)
+ * When out_f64 != NULL the unrounded sum is returned too.                    */
+int orc_sum_partials(const uint16_t *const *partials, int tp, int64_t ldp,
+                     int64_t m, int64_t n, uint16_t *out, double *out_f64)
+{
+    if (!partials || tp < 1 || m < 0 || n < 0 || ldp < n || (!out && !out_f64)) return ORC_ERR_ARG;
+    for (int s = 0; s < tp; ++s)
+        if (!partials[s]) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double acc = 0.0;
+            for (int s = 0; s < tp; ++s)
+                acc += orc_bf16_to_f64(partials[s][i * ldp + j]);
+            if (out) out[i * n + j] = orc_f64_to_bf16(acc);
+            if (out_f64) out_f64[i * n + j] = acc;
+        }
+    return ORC_OK;
+}
+
+/* --------------------------------------- hidden-split RMSNorm (910C layout)
+ * [910C] communication-fusion section: after the cross-rank reduce-add each
+ * rank computes the sum of squares of its own part of the row, the partial
+ * sums are summed across ranks, then the reciprocal root and the normalised
+ * output follow.  Reading R7: rank r owns the column slice [c0, c0 + n_slice)
+ * of every row (the hidden dimension split over ranks), so
+ *   step 1 (per rank):  h[i, j]      = sum_s P_s[i, c0 + j] + residual[i, c0 + j]
+ *                       residual_out = bf16(h)
+ *                       sumsq[i]     = sum_j h[i, j]^2            over the slice
+ *   step 2 (all ranks): ss[i]        = sum_r sumsq_r[i]
+ *                       y[i, j]      = bf16( gamma[c0 + j] * h[i, j] / sqrt(ss[i] / n + eps) )
+ * with n the full hidden size.  Slices taken over all ranks give exactly the
+ * token-chunk epilogue above up to fp64 summation order.
+ * Step 1: partials[s] and residual point at the slice's first column (row stride
+ * ld); residual_out likewise; h_f64 [m][n_slice] and sumsq [m] are outputs.    */
+int orc_reduce_slice_sumsq(const uint16_t *const *partials, int tp, int64_t ld,
+                           int64_t m, int64_t n_slice, const uint16_t *residual,
+                           uint16_t *residual_out, double *h_f64, double *sumsq)
+{
+    if (!partials || tp < 1 || m < 0 || n_slice < 0 || ld < n_slice || !residual || !h_f64 || !sumsq)
+        return ORC_ERR_ARG;
+    for (int s = 0; s < tp; ++s)
+        if (!partials[s]) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < n_slice; ++j) {
+            double acc = 0.0;
+            for (int s = 0; s < tp; ++s)
+                acc += orc_bf16_to_f64(partials[s][i * ld + j]);
+            double h = acc + orc_bf16_to_f64(residual[i * ld + j]);
+            h_f64[i * n_slice + j] = h;
+            if (residual_out) residual_out[i * ld + j] = orc_f64_to_bf16(h);
+            ss += h * h;
+        }
+        sumsq[i] = ss;
+    }
+    return ORC_OK;
+}
+
+/* Step 2: sumsq_parts[r] are the tp ranks' per-row partial sums; gamma points at
+ * the slice's first column; y has row stride ld.                            */
+int orc_rmsnorm_slice_apply(const double *h_f64, const double *const *sumsq_parts, int tp,
+                            int64_t m, int64_t n_slice, int64_t n_total,
+                            const uint16_t *gamma, float eps, uint16_t *y, int64_t ld,
+                            double *y_f64)
+{
+    if (!h_f64 || !sumsq_parts || tp < 1 || m < 0 || n_slice < 0 || n_total < 1 || !gamma ||
+        !(eps >= 0.0f) || ld < n_slice || (!y && !y_f64))
+        return ORC_ERR_ARG;
+    for (int r = 0; r < tp; ++r)
+        if (!sumsq_parts[r]) return ORC_ERR_ARG;
+    const double deps = (double)eps;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+        double ss = 0.0;
+        for (int r = 0; r < tp; ++r) ss += sumsq_parts[r][i];
+        const double denom = sqrt(ss / (double)n_total + deps);
+        for (int64_t j = 0; j < n_slice; ++j) {
+            double v = orc_bf16_to_f64(gamma[j]) * h_f64[i * n_slice + j] / denom;
+            if (y) y[i * ld + j] = orc_f64_to_bf16(v);
+            if (y_f64) y_f64[i * n_slice + j] = v;
+        }
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------- per-token dynamic int8 quantiser

@@ -310,6 +310,65 @@ def check_w8a8_overflow(orc):
     raise AssertionError("int32 overflow not reported")
 
 
+# ------------------------------------------------- all-reduce form, hidden split
+def check_sum_partials(orc):
+    """Exact rational sums; permutation invariance (a sum of at most 16 bf16 values is exact in
+    fp64, so the bf16 result is unique); integer partials exact; TP=1 is the identity."""
+    rng = np.random.default_rng(55)
+    for tp in (1, 2, 3, 5):
+        parts = [_bits(rng.standard_normal((3, 5)).astype(np.float32) * np.float32(10.0 ** rng.integers(-3, 4)))
+                 for _ in range(tp)]
+        out, of = orc.sum_partials(parts, want_f64=True)
+        for i in range(3):
+            for j in range(5):
+                exact = sum(bf16_value(p[i, j]) for p in parts)
+                assert Fraction(of[i, j]) == exact
+                assert int(out[i, j]) == exact_bf16(exact), (tp, i, j)
+        perm = orc.sum_partials(parts[::-1])
+        assert np.array_equal(perm, out)
+        if tp == 1:
+            assert np.array_equal(out, parts[0])
+    ints = [_bits(rng.integers(-50, 51, (4, 8)).astype(np.float32)) for _ in range(4)]
+    want = sum(synth.bf16_decode(p).astype(np.float64) for p in ints)
+    assert np.array_equal(synth.bf16_decode(orc.sum_partials(ints)).astype(np.float64), want)
+
+
+def check_hidden_split_epilogue(orc):
+    """Hidden-split epilogue: the column slices of all ranks reproduce the pinned token-chunk
+    epilogue (residual_out bit-exact, y to fp64 rounding), the slice sums of squares are exact
+    rational sums, and the partition does not matter."""
+    rng = np.random.default_rng(56)
+    m, n, tp = 5, 48, 3
+    parts = [_bits(rng.standard_normal((m, n)).astype(np.float32)) for _ in range(tp)]
+    res = _bits(rng.standard_normal((m, n)).astype(np.float32))
+    gam = _bits(rng.uniform(0.5, 1.5, n).astype(np.float32))
+    eps = 1e-6
+    y_ref, ro_ref, h_ref, y_ref64 = orc.reduce_chunk_rmsnorm(parts, res, gam, eps, want_f64=True)
+    for bounds in ([0, 16, 40, 48], [0, 8, 16, 24, 32, 40, 48], [0, 48]):
+        slices = list(zip(bounds[:-1], bounds[1:]))
+        step1 = [orc.reduce_slice_sumsq(parts, res, a, b - a) for a, b in slices]
+        ss_parts = [st[2] for st in step1]
+        ro = np.concatenate([st[0] for st in step1], axis=1)
+        assert np.array_equal(ro, ro_ref), bounds
+        assert np.allclose(np.sum(ss_parts, axis=0), np.sum(h_ref ** 2, axis=1), rtol=1e-13, atol=0)
+        ys = [orc.rmsnorm_slice_apply(st[1], ss_parts, n, gam[a:b], eps, want_f64=True) for st, (a, b) in
+              zip(step1, slices)]
+        y64 = np.concatenate([yy[1] for yy in ys], axis=1)
+        assert np.allclose(y64, y_ref64, rtol=1e-12, atol=0), bounds
+        y = np.concatenate([yy[0] for yy in ys], axis=1)
+        flips = np.flatnonzero(y != y_ref)
+        assert flips.size <= 1, f"{flips.size} bf16 results differ beyond fp64 summation order"
+    # exact rational sum of squares of one slice
+    ro, h, ss = orc.reduce_slice_sumsq(parts, res, 8, 12)
+    for i in range(m):
+        exact = Fraction(0)
+        for j in range(8, 20):
+            hv = sum(bf16_value(p[i, j]) for p in parts) + bf16_value(res[i, j])
+            assert Fraction(h[i, j - 8]) == hv
+            exact += hv * hv
+        assert abs(Fraction(ss[i]) - exact) <= exact * Fraction(1, 2 ** 48)
+
+
 # ------------------------------------------------------- per-token quantiser
 def _f32_nearest(v: Fraction) -> np.float32:
     """The float32 nearest to an exact rational (ties to even), by neighbour search."""
@@ -423,5 +482,6 @@ ALL_CHECKS = [
     check_partial_one_hot, check_partial_small_integers, check_partial_padding_and_chunks,
     check_reduce_bruteforce, check_rms_invariant, check_unit_rms_and_scale_invariance,
     check_zero_row_and_tp1, check_integer_partials_exact, check_w8a8, check_w8a8_overflow,
-    check_quant_exact, check_quant_properties, check_golden,
+    check_sum_partials, check_hidden_split_epilogue, check_quant_exact, check_quant_properties,
+    check_golden,
 ]

@@ -5,7 +5,9 @@ The second half plants plausible mistakes in copies of the oracle's C source
 the root, ties rounded away from zero, a missing subnormal clamp, a dropped
 residual, a reordered dequantisation, a quantiser that rounds ties away from
 zero, truncates, divides by 128, drops the absolute value or the last column,
-or gives a zero row scale 1), compiles each copy with gcc and checks that at
+or gives a zero row scale 1; an all-reduce sum that drops a shard; a
+hidden-split epilogue that sums h instead of h^2, averages over the slice or
+drops a rank), compiles each copy with gcc and checks that at
 least one pin fails for every one of them.
 """
 import os
@@ -64,6 +66,15 @@ MUTANTS = [
     ("dequant_scales_multiplied_first",
      "volatile float v = u * sw[j];",
      "volatile float v = t * (((r < m) ? sx[r] : 0.0f) * sw[j]);"),
+    ("sum_partials_drops_shard_0",
+     "for (int s = 0; s < tp; ++s)\n                acc += orc_bf16_to_f64(partials[s][i * ldp + j]);\n            if (out) out[i * n + j]",
+     "for (int s = 1; s < tp; ++s)\n                acc += orc_bf16_to_f64(partials[s][i * ldp + j]);\n            if (out) out[i * n + j]"),
+    ("slice_sum_of_h_not_squares", "            ss += h * h;\n        }\n        sumsq[i] = ss;",
+     "            ss += h;\n        }\n        sumsq[i] = ss;"),
+    ("slice_mean_over_slice_width", "const double denom = sqrt(ss / (double)n_total + deps);",
+     "const double denom = sqrt(ss / (double)n_slice + deps);"),
+    ("slice_drops_last_rank", "for (int r = 0; r < tp; ++r) ss += sumsq_parts[r][i];",
+     "for (int r = 0; r + 1 < tp; ++r) ss += sumsq_parts[r][i];"),
     ("quant_ties_away_from_zero", "float v = nearbyintf(t);", "float v = roundf(t);"),
     ("quant_scale_over_128", "volatile float s = amax / 127.0f;", "volatile float s = amax / 128.0f;"),
     ("quant_absmax_without_abs", "float a = fabsf((float)orc_bf16_to_f64(xr[kk]));",
