@@ -186,6 +186,68 @@ rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
                             void *stream);
 
 /*
+ * rpl_sum_partials -- the all-reduce form of the cross-rank sum (no epilogue).
+ *
+ * [MMAR] PR description: RowParallelLinear's matmul is fused with its
+ * all-reduce, after which every rank holds the sum of all ranks' partials for
+ * all token rows.  On one GPU the tp partials are given directly:
+ *   out[i, j] = bf16_rne( sum_s partials[s][i, j] )        (fp32 sum, shard order)
+ *
+ * partials  HOST array of tp DEVICE pointers, each -> [m, n] bf16, row stride ldp
+ * out       [m, n] bf16 contiguous; must not overlap a partial
+ *
+ * RPL_ERR_NULL        partials is NULL, or m > 0 and out or a partials[s] is NULL
+ * RPL_ERR_INVALID     tp < 1, m < 0, n < 1, ldp < n, out overlaps a partial
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; n or ldp not a multiple of 8; pointers
+ *                     not 16-byte aligned; m or n >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_sum_partials(const rpl_bf16 *const *partials, int32_t tp, int64_t m, int64_t n,
+                            int64_t ldp, rpl_bf16 *out, void *stream);
+
+/*
+ * rpl_reduce_slice_sumsq / rpl_rmsnorm_slice_apply -- the hidden-split epilogue
+ * of the 910C layout, where each rank owns a column slice of every token row.
+ *
+ * [910C] communication-fusion section: after the cross-rank reduce-add each
+ * rank takes the sum of squares of its part of the row, those partial sums are
+ * summed across ranks, then the reciprocal root and the normalised output.
+ *
+ * Step 1, rank r on its slice (columns c0 .. c0 + n_slice - 1):
+ *   h[i, j]      = sum_s partials[s][i, j] + residual[i, j]     (fp32)
+ *   residual_out = bf16_rne(h);   h_out[i, j] = h (fp32);   sumsq[i] = sum_j h[i, j]^2
+ * partials[s], residual, residual_out point at the slice's first column of
+ * [m, *] arrays with row stride ld; h_out [m, n_slice] fp32 contiguous; sumsq
+ * [m] fp32.  residual_out may be exactly residual.
+ *
+ * Step 2, after the cross-rank sum (emulated here: the tp ranks' sumsq arrays
+ * are summed by the kernel):
+ *   ss[i] = sum_r sumsq_parts[r][i];   y[i, j] = bf16_rne(gamma[j] * h[i, j] / sqrt(ss[i] / n_total + eps))
+ * h [m, n_slice] fp32 from step 1; gamma -> the slice's n_slice weights; y
+ * points at the slice's first column, row stride ld; n_total is the full
+ * hidden size.  Over all ranks' slices this equals rpl_reduce_chunk_rmsnorm's
+ * outputs (to fp32 summation order).
+ *
+ * RPL_ERR_NULL        an array or required pointer is NULL (m > 0)
+ * RPL_ERR_INVALID     tp < 1, m < 0, n_slice < 1, ld < n_slice, n_total < n_slice,
+ *                     eps < 0 or not finite, an output overlaps an input or
+ *                     another output (residual_out == residual allowed)
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; n_slice or ld not a multiple of 8;
+ *                     n_slice > 16384; bf16 and fp32 row pointers not 16-byte
+ *                     aligned (sumsq arrays: 4-byte); m >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_reduce_slice_sumsq(const rpl_bf16 *const *partials, int32_t tp, int64_t m,
+                                  int64_t n_slice, int64_t ld, const rpl_bf16 *residual,
+                                  rpl_bf16 *residual_out, float *h_out, float *sumsq,
+                                  void *stream);
+
+rpl_status rpl_rmsnorm_slice_apply(const float *h, const float *const *sumsq_parts, int32_t tp,
+                                   int64_t m, int64_t n_slice, int64_t n_total,
+                                   const rpl_bf16 *gamma, float eps, rpl_bf16 *y, int64_t ld,
+                                   void *stream);
+
+/*
  * rpl_quant_per_token -- per-token dynamic int8 quantisation of a bf16
  * activation, the producer of rpl_w8a8_partial's xq and x_scale.
  *
@@ -269,7 +331,7 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 1.2. */
+/* Library ABI version: (major << 16) | minor.  Currently 1.3. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

@@ -15,6 +15,9 @@ the library is missing, every call raises.
     rpl_quant_per_token(x)                     -> (xq int8, x_scale fp32)
     rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps)
                                                -> (y, residual_out), one launch
+    rpl_sum_partials(partials)                 -> bf16 sum (all-reduce form)
+    rpl_reduce_slice_sumsq / rpl_rmsnorm_slice_apply
+                                               hidden-split epilogue, two steps
 """
 from __future__ import annotations
 
@@ -57,6 +60,12 @@ def lib() -> ctypes.CDLL:
         L.rpl_matmul_reduce_rmsnorm.restype = ctypes.c_int
         L.rpl_matmul_reduce_rmsnorm.argtypes = [_p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _p,
                                                 ctypes.c_float, _p, _p, _p, _i64, _p]
+        L.rpl_sum_partials.restype = ctypes.c_int
+        L.rpl_sum_partials.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _p]
+        L.rpl_reduce_slice_sumsq.restype = ctypes.c_int
+        L.rpl_reduce_slice_sumsq.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _p, _p, _p, _p]
+        L.rpl_rmsnorm_slice_apply.restype = ctypes.c_int
+        L.rpl_rmsnorm_slice_apply.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p]
         L.rpl_quant_per_token.restype = ctypes.c_int
         L.rpl_quant_per_token.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
@@ -226,6 +235,80 @@ def rpl_quant_per_token(x, xq=None, x_scale=None, stream=None):
     return xq, x_scale
 
 
+def _ptrs(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return arr, ctypes.cast(arr, _p)
+
+
+def rpl_sum_partials(partials, out=None, stream=None):
+    """All-reduce form: bf16 sum of the tp [m, n] bf16 partials (same row stride)."""
+    torch = _torch()
+    for i, t in enumerate(partials):
+        _dev(t, f"partials[{i}]", torch.bfloat16, 2)
+    m, n = partials[0].shape
+    ldp = _ld(partials[0])
+    if any(t.shape != (m, n) or _ld(t) != ldp for t in partials):
+        raise ValueError("partials must share shape and row stride")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=partials[0].device)
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (m, n) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{m}, {n}] tensor")
+    keep, arr = _ptrs(partials)
+    st = lib().rpl_sum_partials(arr, len(partials), m, n, ldp, out.data_ptr(), _stream(out, stream))
+    _check("rpl_sum_partials", st)
+    return out
+
+
+def rpl_reduce_slice_sumsq(partials, residual, residual_out, h=None, sumsq=None, stream=None):
+    """Hidden-split step 1 on one column slice.  partials, residual and residual_out are
+    [m, n_slice] views sharing one row stride (e.g. full[:, c0:c0 + n_slice]).
+    Returns (h fp32 [m, n_slice], sumsq fp32 [m])."""
+    torch = _torch()
+    for i, t in enumerate(partials):
+        _dev(t, f"partials[{i}]", torch.bfloat16, 2)
+    _dev(residual, "residual", torch.bfloat16, 2)
+    _dev(residual_out, "residual_out", torch.bfloat16, 2)
+    m, ns = residual.shape
+    ld = _ld(residual)
+    views = list(partials) + [residual_out]
+    if any(t.shape != (m, ns) or _ld(t) != ld for t in views):
+        raise ValueError("slices must share shape and row stride")
+    if h is None:
+        h = torch.empty((m, ns), dtype=torch.float32, device=residual.device)
+    if sumsq is None:
+        sumsq = torch.empty((m,), dtype=torch.float32, device=residual.device)
+    _dev(h, "h", torch.float32, 2)
+    _dev(sumsq, "sumsq", torch.float32, 1)
+    if tuple(h.shape) != (m, ns) or not h.is_contiguous() or sumsq.shape[0] != m:
+        raise ValueError("h must be a contiguous [m, n_slice] fp32 tensor and sumsq [m]")
+    keep, arr = _ptrs(partials)
+    st = lib().rpl_reduce_slice_sumsq(arr, len(partials), m, ns, ld, residual.data_ptr(), residual_out.data_ptr(),
+                                      h.data_ptr(), sumsq.data_ptr(), _stream(residual, stream))
+    _check("rpl_reduce_slice_sumsq", st)
+    return h, sumsq
+
+
+def rpl_rmsnorm_slice_apply(h, sumsq_parts, n_total: int, gamma, eps: float, y, stream=None):
+    """Hidden-split step 2: y (an [m, n_slice] bf16 view) = gamma * h / sqrt(sum_r sumsq_r / n_total + eps)."""
+    torch = _torch()
+    _dev(h, "h", torch.float32, 2)
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    _dev(y, "y", torch.bfloat16, 2)
+    m, ns = h.shape
+    for i, t in enumerate(sumsq_parts):
+        _dev(t, f"sumsq_parts[{i}]", torch.float32, 1)
+        if t.shape[0] != m:
+            raise ValueError("each sumsq part has m entries")
+    if tuple(y.shape) != (m, ns) or gamma.shape[0] != ns or not h.is_contiguous():
+        raise ValueError("shape mismatch")
+    keep, arr = _ptrs(sumsq_parts)
+    st = lib().rpl_rmsnorm_slice_apply(h.data_ptr(), arr, len(sumsq_parts), m, ns, n_total, gamma.data_ptr(),
+                                       float(eps), y.data_ptr(), _ld(y), _stream(h, stream))
+    _check("rpl_rmsnorm_slice_apply", st)
+    return y
+
+
 def rpl_matmul_reduce_rmsnorm_workspace(m: int, n: int, device=None):
     """A zero-filled workspace for rpl_matmul_reduce_rmsnorm on [m, n] (reusable across calls)."""
     torch = _torch()
@@ -280,6 +363,7 @@ def rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps: float, w
 
 
 __all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
-           "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace",
+           "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace", "rpl_sum_partials",
+           "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
            "rpl_status_string", "rpl_version",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

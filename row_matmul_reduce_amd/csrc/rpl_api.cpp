@@ -131,6 +131,97 @@ rpl_status rpl_w8a8_partial(const int8_t *xq, int64_t ldx, const float *x_scale,
                                                   (int)n, (int)k, static_cast<hipStream_t>(stream)));
 }
 
+rpl_status rpl_sum_partials(const rpl_bf16 *const *partials, int32_t tp, int64_t m, int64_t n, int64_t ldp,
+                            rpl_bf16 *out, void *stream) {
+    if (!partials) return RPL_ERR_NULL;
+    if (m != 0) {
+        if (!out) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!partials[s]) return RPL_ERR_NULL;
+    }
+    if (tp < 1 || m < 0 || n < 1 || ldp < n) return RPL_ERR_INVALID;
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    const int64_t ob = span(m, n, n, 2), pb = span(m, n, ldp, 2);
+    for (int s = 0; s < np; ++s)
+        if (overlap(out, ob, partials[s], pb)) return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || n % 8 || ldp % 8 || !aligned(out, 16)) return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp; ++s)
+        if (!aligned(partials[s], 16)) return RPL_ERR_UNSUPPORTED;
+    if (m > kMaxDim || n > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    rpl::PartialPtrs p{};
+    for (int s = 0; s < tp; ++s) p.p[s] = partials[s];
+    return launch_status(rpl::launch_sum_partials(p, tp, (int)m, (int)n, ldp, out, static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_reduce_slice_sumsq(const rpl_bf16 *const *partials, int32_t tp, int64_t m, int64_t n_slice,
+                                  int64_t ld, const rpl_bf16 *residual, rpl_bf16 *residual_out, float *h_out,
+                                  float *sumsq, void *stream) {
+    if (!partials) return RPL_ERR_NULL;
+    if (m != 0) {
+        if (!residual || !residual_out || !h_out || !sumsq) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!partials[s]) return RPL_ERR_NULL;
+    }
+    if (tp < 1 || m < 0 || n_slice < 1 || ld < n_slice) return RPL_ERR_INVALID;
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    const int64_t sl = span(m, n_slice, ld, 2), hb = span(m, n_slice, n_slice, 4), sb = span(1, m, m, 4);
+    const void *outs[3] = {residual_out, h_out, sumsq};
+    const int64_t osz[3] = {sl, hb, sb};
+    for (int o = 0; o < 3; ++o) {
+        if (o != 0 || residual_out != residual)
+            if (overlap(outs[o], osz[o], residual, sl)) return RPL_ERR_INVALID;
+        for (int s = 0; s < np; ++s)
+            if (overlap(outs[o], osz[o], partials[s], sl)) return RPL_ERR_INVALID;
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], osz[o], outs[q], osz[q])) return RPL_ERR_INVALID;
+    }
+    if (tp > RPL_MAX_TP || n_slice % 8 || ld % 8 || n_slice > 16384) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(residual, 16) || !aligned(residual_out, 16) || !aligned(h_out, 16) || !aligned(sumsq, 4))
+        return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp; ++s)
+        if (!aligned(partials[s], 16)) return RPL_ERR_UNSUPPORTED;
+    if (m > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    rpl::PartialPtrs p{};
+    for (int s = 0; s < tp; ++s) p.p[s] = partials[s];
+    return launch_status(rpl::launch_slice_sumsq(p, tp, (int)m, (int)n_slice, ld, residual, residual_out, h_out,
+                                                 sumsq, static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_rmsnorm_slice_apply(const float *h, const float *const *sumsq_parts, int32_t tp, int64_t m,
+                                   int64_t n_slice, int64_t n_total, const rpl_bf16 *gamma, float eps, rpl_bf16 *y,
+                                   int64_t ld, void *stream) {
+    if (!sumsq_parts || !gamma) return RPL_ERR_NULL;
+    if (m != 0) {
+        if (!h || !y) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!sumsq_parts[s]) return RPL_ERR_NULL;
+    }
+    if (tp < 1 || m < 0 || n_slice < 1 || ld < n_slice || n_total < n_slice || !(eps >= 0.0f) ||
+        !std::isfinite(eps))
+        return RPL_ERR_INVALID;
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    const int64_t yb = span(m, n_slice, ld, 2);
+    if (overlap(y, yb, h, span(m, n_slice, n_slice, 4)) || overlap(y, yb, gamma, span(1, n_slice, n_slice, 2)))
+        return RPL_ERR_INVALID;
+    for (int s = 0; s < np; ++s)
+        if (overlap(y, yb, sumsq_parts[s], span(1, m, m, 4))) return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || n_slice % 8 || ld % 8 || n_slice > 16384) return RPL_ERR_UNSUPPORTED;
+    if (!aligned(h, 16) || !aligned(gamma, 16) || !aligned(y, 16)) return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp; ++s)
+        if (!aligned(sumsq_parts[s], 4)) return RPL_ERR_UNSUPPORTED;
+    if (m > kMaxDim || n_total > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    rpl::SumsqPtrs sp{};
+    for (int s = 0; s < tp; ++s) sp.p[s] = sumsq_parts[s];
+    return launch_status(rpl::launch_slice_apply(h, sp, tp, (int)m, (int)n_slice, (int)n_total, gamma, eps, y, ld,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx, int8_t *xq, int64_t ldq, float *x_scale, int64_t m,
                                int64_t k, void *stream) {
     if (m != 0 && (!x || !xq || !x_scale)) return RPL_ERR_NULL;
@@ -228,6 +319,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (1 << 16) | 2; }
+int32_t rpl_version(void) { return (1 << 16) | 3; }
 
 }  // extern "C"

@@ -12,6 +12,9 @@ constexpr int MAX_TP = 16;
 struct PartialPtrs {
     const uint16_t *p[MAX_TP];
 };
+struct SumsqPtrs {
+    const float *p[MAX_TP];
+};
 
 hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw, uint16_t *out,
                                int m, int m_pad, int n, int k, hipStream_t st);
@@ -42,6 +45,13 @@ struct FusedDecodeArgs {
 int64_t fused_decode_workspace_bytes(int64_t m, int64_t n);
 int64_t fused_decode_ss_bytes(int64_t m, int64_t n);
 hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st);
+
+hipError_t launch_sum_partials(const PartialPtrs &p, int tp, int m, int n, int64_t ldp, uint16_t *out,
+                               hipStream_t st);
+hipError_t launch_slice_sumsq(const PartialPtrs &p, int tp, int m, int ns, int64_t ld, const uint16_t *residual,
+                              uint16_t *residual_out, float *h, float *sumsq, hipStream_t st);
+hipError_t launch_slice_apply(const float *h, const SumsqPtrs &s, int tp, int m, int ns, int n_total,
+                              const uint16_t *gamma, float eps, uint16_t *y, int64_t ld, hipStream_t st);
 
 hipError_t launch_quant_per_token(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq, float *scale, int m,
                                   int k, hipStream_t st);

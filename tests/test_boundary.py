@@ -32,6 +32,7 @@ def test_header_declares_the_path_calls():
     names = declared_functions()
     for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
               "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace_size",
+              "rpl_sum_partials", "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
               "rpl_status_string", "rpl_version"):
         assert f in names
 
@@ -51,7 +52,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (1 << 16) | 2
+    assert rpl.rpl_version() == (1 << 16) | 3
 
 
 class Buf:
@@ -282,6 +283,65 @@ def test_fused_decode_validation():
     for b in (X0, X1, W0, W1, R, G, Y, RO, WS):
         assert b.untouched()
     assert case(m=0, mv=0, res=None, y=None, ro=None, work=None, wbytes=0) == OK
+
+
+def _parr(ptrs):
+    import ctypes
+    return ctypes.cast((ctypes.c_void_p * len(ptrs))(*ptrs), ctypes.c_void_p)
+
+
+def test_sum_partials_validation():
+    L = rpl.lib()
+    m, n, tp = 3, 64, 2
+    P0, P1, O = Buf(m * n * 2), Buf(m * n * 2), Buf(m * n * 2)
+    p, o = [P0.ptr, P1.ptr], O.ptr
+    call = lambda ps, tp_, m_, n_, ld, out: L.rpl_sum_partials(_parr(ps) if ps is not None else None, tp_, m_, n_,
+                                                              ld, out, None)
+    cases = [((None, tp, m, n, n, o), NULL), (([P0.ptr, None], tp, m, n, n, o), NULL), ((p, tp, m, n, n, None), NULL),
+             ((p, 0, m, n, n, o), INVALID), ((p, tp, -1, n, n, o), INVALID), ((p, tp, m, 0, n, o), INVALID),
+             ((p, tp, m, n, 56, o), INVALID), ((p, tp, m, n, n, P1.ptr + 32), INVALID),
+             ((p * 9, 17, m, n, n, o), UNSUP), ((p, tp, m, 60, 64, o), UNSUP), ((p, tp, m, n, 68, o), UNSUP),
+             ((p, tp, m, n, n, o + 8), UNSUP), (([P0.ptr + 8, P1.ptr], tp, m, n, n, o), UNSUP)]
+    for args, want in cases:
+        assert call(*args) == want, args
+    for b in (P0, P1, O):
+        assert b.untouched()
+    assert call([None, None], tp, 0, n, n, None) == OK
+
+
+def test_hidden_split_validation():
+    L = rpl.lib()
+    m, ns, ld, tp = 3, 32, 64, 2
+    P0, P1, R, RO = Buf(m * ld * 2), Buf(m * ld * 2), Buf(m * ld * 2), Buf(m * ld * 2)
+    H, S0, S1, G, Y = Buf(m * ns * 4), Buf(m * 4), Buf(m * 4), Buf(ns * 2), Buf(m * ld * 2)
+    p = [P0.ptr, P1.ptr]
+    s1 = lambda ps, tp_, m_, ns_, ld_, r, ro, h, ss: L.rpl_reduce_slice_sumsq(
+        _parr(ps) if ps is not None else None, tp_, m_, ns_, ld_, r, ro, h, ss, None)
+    base1 = (p, tp, m, ns, ld, R.ptr, RO.ptr, H.ptr, S0.ptr)
+    c1 = [((None,) + base1[1:], NULL), (base1[:5] + (None,) + base1[6:], NULL), (base1[:8] + (None,), NULL),
+          ((p, 0) + base1[2:], INVALID), ((p, tp, m, 0) + base1[4:], INVALID), ((p, tp, m, ns, 24) + base1[5:], INVALID),
+          (base1[:6] + (P0.ptr + 16,) + base1[7:], INVALID), (base1[:7] + (RO.ptr,) + base1[8:], INVALID),
+          (base1[:8] + (H.ptr + 8,), INVALID), ((p * 9, 17) + base1[2:], UNSUP), ((p, tp, m, 36, ld) + base1[5:], UNSUP),
+          ((p, tp, m, ns, 68) + base1[5:], UNSUP), (base1[:7] + (H.ptr + 8, S0.ptr), UNSUP),
+          ((p, tp, m, 16392, 16392, 1 << 40, 1 << 41, 1 << 42, 1 << 43), UNSUP)]
+    for args, want in c1:
+        assert s1(*args) == want, args
+    s2 = lambda h, sp, tp_, m_, ns_, nt, g, eps, y, ld_: L.rpl_rmsnorm_slice_apply(
+        h, _parr(sp) if sp is not None else None, tp_, m_, ns_, nt, g, eps, y, ld_, None)
+    sp = [S0.ptr, S1.ptr]
+    base2 = (H.ptr, sp, tp, m, ns, 64, G.ptr, 1e-6, Y.ptr, ld)
+    c2 = [((H.ptr, None) + base2[2:], NULL), (base2[:6] + (None,) + base2[7:], NULL), ((None,) + base2[1:], NULL),
+          (base2[:8] + (None, ld), NULL), ((H.ptr, [S0.ptr, None]) + base2[2:], NULL),
+          (base2[:5] + (16,) + base2[6:], INVALID), (base2[:7] + (-1.0,) + base2[8:], INVALID),
+          (base2[:9] + (16,), INVALID), (base2[:8] + (H.ptr, ld), INVALID),
+          (base2[:4] + (36,) + base2[5:], UNSUP), (base2[:8] + (Y.ptr + 8, ld), UNSUP),
+          ((H.ptr + 4,) + base2[1:], UNSUP), ((H.ptr, [S0.ptr + 2, S1.ptr]) + base2[2:], UNSUP)]
+    for args, want in c2:
+        assert s2(*args) == want, args
+    for b in (P0, P1, R, RO, H, S0, S1, G, Y):
+        assert b.untouched()
+    assert s1([None, None], tp, 0, ns, ld, None, None, None, None) == OK
+    assert s2(None, sp, tp, 0, ns, 64, G.ptr, 1e-6, None, ld) == OK
 
 
 def test_binding_rejects_host_tensors():
