@@ -19,7 +19,8 @@ so each precision is its own path.  The default run times the bf16 prefill down_
 the w8a8 twin, the decode o_proj share and the TP=8 long-prefill share as side
 steps (w8a8 both from int8 inputs and from the bf16 activation), plus the
 single-launch decode path (every shard's product + sum + residual + RMSNorm in one
-kernel) for a token chunk and for all rows.  Every step cycles through several copies of its inputs (more than
+kernel) for a token chunk and for all rows, the all-reduce sum and the hidden-split
+epilogue.  Every step cycles through several copies of its inputs (more than
 twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
@@ -52,6 +53,7 @@ KERNEL_SOURCES = {
     "reduce_rmsnorm": ["reduce_rmsnorm.hip", "rpl_device.h"],
     "quant_per_token": ["quant_per_token.hip", "rpl_device.h"],
     "decode_fused": ["decode_fused.hip", "rpl_device.h"],
+    "reduce_variants": ["reduce_variants.hip", "rpl_device.h"],
 }
 WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
@@ -288,6 +290,80 @@ def fused_decode(torch, rpl, copies: int, all_rows: bool, launches: int = 200):
             "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "weight_sets_rotated": len(sets)}
 
 
+def _graph_mean_us(torch, fn, n_sets: int, launches: int = 100):
+    """Mean device time per launch of fn(i) over a replayed HIP graph of `launches` launches
+    (small kernels: a Python launch costs more than the kernel, so events around single
+    launches would time the host)."""
+    for i in range(max(3, n_sets)):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / launches
+
+
+def reduce_variants(torch, rpl, copies: int):
+    """The other reduction forms on the pages' shapes, HBM-resident: the all-reduce sum of the
+    prefill down_proj partials (all 4096 rows, TP=2) and the hidden-split epilogue for rank 0's
+    column slice of the TP=8 long-prefill chunk (2048 rows, 640 of 5120 columns)."""
+    from row_matmul_reduce_amd import synth
+    rng = np.random.default_rng(0)
+
+    def bf(shape):
+        return torch.from_numpy(synth.bf16_bits(rng.standard_normal(shape, dtype=np.float32)).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    out = {}
+    wl = synth.WORKLOADS[WORKLOAD_IDS["prefill"]]
+    m, n, tp = wl.m, wl.n, wl.tp
+    base = [bf((m, n)) for _ in range(tp)]
+    nb = tp * m * n * 2
+    k = copies if copies > 0 else max(3, -(-(2 * MALL_BYTES + 1) // nb) + 1)
+    sets = [base] + [[t.clone() for t in base] for _ in range(k - 1)]
+    o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    us = _graph_mean_us(torch, lambda i: rpl.rpl_sum_partials(sets[i % len(sets)], out=o), len(sets))
+    b = (tp + 1) * m * n * 2
+    out["allreduce_sum"] = {"workload": wl.name, "rows": m, "shards": tp, "us": us, "bytes": b,
+                            "GB/s": b / (us * 1e-6) / 1e9, "frac_hbm": b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                            "input_sets_rotated": len(sets)}
+    del sets, base
+    wl = synth.WORKLOADS[WORKLOAD_IDS["long_prefill"]]
+    m, n, tp = wl.m_chunk, wl.n, wl.tp
+    ns = n // tp
+    base = [bf((m, n)) for _ in range(tp)] + [bf((m, n))]
+    nb = (tp + 1) * m * n * 2
+    k = copies if copies > 0 else max(3, -(-(2 * MALL_BYTES + 1) // nb) + 1)
+    sets = [base] + [[t.clone() for t in base] for _ in range(k - 1)]
+    ro = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    h = torch.empty((m, ns), dtype=torch.float32, device="cuda")
+    ss = [torch.rand(m, dtype=torch.float32, device="cuda") * ns for _ in range(tp)]
+    gam = bf((n,))
+
+    def step1(i):
+        d = sets[i % len(sets)]
+        rpl.rpl_reduce_slice_sumsq([p[:, :ns] for p in d[:tp]], d[tp][:, :ns], ro[:, :ns], h=h, sumsq=ss[0])
+
+    us1 = _graph_mean_us(torch, step1, len(sets))
+    us2 = _graph_mean_us(torch, lambda i: rpl.rpl_rmsnorm_slice_apply(h, ss, n, gam[:ns], wl.eps, y[:, :ns]), 1)
+    b1 = tp * m * ns * 2 + 2 * m * ns * 2 + m * ns * 4 + 4 * m
+    b2 = m * ns * 4 + tp * 4 * m + ns * 2 + m * ns * 2
+    out["hidden_split_slice"] = {"workload": wl.name, "rows": m, "slice_cols": ns, "shards": tp,
+                                 "step1_us": us1, "step1_bytes": b1, "step1_GB/s": b1 / (us1 * 1e-6) / 1e9,
+                                 "step2_us": us2, "step2_bytes": b2, "step2_GB/s": b2 / (us2 * 1e-6) / 1e9,
+                                 "input_sets_rotated": len(sets)}
+    return out
+
+
 def library_reference(path, torch, steps: int):
     """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
     HBM-resident input sets, same stream and timing method, to show what the chip gives under the
@@ -420,6 +496,8 @@ def main():
         for key, all_rows in (("decode_fused_chunk", False), ("decode_fused_allreduce", True)):
             side[key] = fused_decode(torch, rpl, args.copies, all_rows)
             torch.cuda.empty_cache()
+        side.update(reduce_variants(torch, rpl, args.copies))
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline and wl.kind != "w8a8":
