@@ -55,6 +55,8 @@ KERNEL_SOURCES = {
     "decode_fused": ["decode_fused.hip", "rpl_device.h"],
     "reduce_variants": ["reduce_variants.hip", "rpl_device.h"],
 }
+# kernels that live in a shared source file
+KERNEL_KEY = {"sum_partials": "reduce_variants", "slice_sumsq": "reduce_variants", "slice_apply": "reduce_variants"}
 WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
 
@@ -77,7 +79,7 @@ def load_traffic(kernel_key: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f).get(f"{kernel_key}@{workload}")
-    if not rec or rec.get("source_sha256_16") != kernel_source_hash(kernel_key):
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(KERNEL_KEY.get(kernel_key, kernel_key)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
