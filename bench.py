@@ -201,19 +201,24 @@ class Path:
         return wall * 1e3 / steps, kern, kern[self.pname]
 
     def run(self, steps: int, warmup: int):
-        """Time `steps` steps after `warmup`: wall ms per step, per-kernel HIP event means (us),
-        and the back-to-back launch period of the partial alone (us; includes launch gaps)."""
+        """Time `steps` steps after `warmup`: wall ms per step (the steps alone, nothing recorded
+        between their kernels), then the same number of steps again with HIP events around each
+        kernel for the per-kernel means (us), and the back-to-back launch period of the partial
+        alone (us; includes launch gaps)."""
         torch = self.torch
         for i in range(warmup):
             self.step(i)
-        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in self.names]
-               for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(warmup + i, evs[i])
+            self.step(warmup + i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in self.names]
+               for _ in range(steps)]
+        for i in range(steps):
+            self.step(warmup + steps + i, evs[i])
+        torch.cuda.synchronize()
         kern = {nm: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
                 for j, nm in enumerate(self.names)}
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
