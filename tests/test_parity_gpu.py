@@ -198,6 +198,32 @@ def test_received_chunk_end_to_end(wid):
     say(f"  max abs err residual_out {e1:.3g} y {e2:.3g} over {rows.size} rows")
 
 
+def test_partial_row_stride_at_the_limit():
+    """Row strides just under the 8 MiB the tile engine's 32-bit buffer offsets allow
+    (255 rows x stride must stay below 2^31 bytes): a 256-row tile's last rows are read."""
+    import torch
+    m, n, k = 300, 264, 64
+    ldx = (1 << 22) - 8                      # elements: 8 MiB - 16 bytes per row
+    rng = np.random.default_rng(21)
+    x = synth.bf16_bits(rng.standard_normal((m, k), dtype=np.float32) / np.float32(8.0))
+    w = synth.bf16_bits(rng.standard_normal((n, k), dtype=np.float32) / np.float32(8.0))
+    say(f"[partial ld limit] m={m} ldx={ldx}")
+    big = torch.zeros((m, ldx), dtype=torch.bfloat16, device="cuda")
+    big[:, :k] = dev_bf16(x)
+    out = rpl.rpl_partial(big[:, :k], dev_bf16(w), 2)
+    assert_bf16_close(host_bf16(out)[:m], oracle.partial_rows(x, w, m), "partial at the stride limit")
+    del big
+    xq = rng.integers(-127, 128, (m, 64), dtype=np.int8)
+    wq = rng.integers(-127, 128, (n, 64), dtype=np.int8)
+    sx = rng.uniform(1e-3, 2e-2, m).astype(np.float32)
+    sw = rng.uniform(1e-3, 1e-2, n).astype(np.float32)
+    bq = torch.zeros((m, (1 << 23) - 16), dtype=torch.int8, device="cuda")
+    bq[:, :64] = dev(xq)
+    _, acc = rpl.rpl_w8a8_partial(bq[:, :64], dev(sx), dev(wq), dev(sw), 2, want_acc=True)
+    _, wacc = oracle.w8a8_rows(xq, sx, wq, sw, m, tp=2)
+    assert np.array_equal(acc.cpu().numpy(), wacc)
+
+
 # ------------------------------------------------------------------------ w8a8
 W8A8_SHAPES = [(64, 512, 256, 2), (5, 24, 32, 2), (17, 40, 64, 8), (300, 520, 672, 2), (257, 264, 272, 4),
                (512, 448, 256, 2), (512, 512, 512, 4), (4100, 4104, 160, 2)]
