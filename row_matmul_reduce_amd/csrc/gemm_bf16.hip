@@ -11,9 +11,9 @@
 // reduce-scatter send layout [tp][M_pad/tp][n]; pad rows are zero.
 //
 // Two kernels:
-//  * prefill: the MFMA tile engine of gemm_nt.h (operands DMA'd straight to
-//    LDS, double-buffered, fragment reads prefetched across the barrier) with
-//    v_mfma_f32_16x16x32_bf16 and fp32 accumulators;
+//  * prefill: the four-wave form of the MFMA tile engine of gemm_nt.h
+//    (256 x 224 tiles, operands DMA'd straight to LDS, double-buffered) with
+//    v_mfma_f32_16x16x32_bf16 and fp32 accumulators in accumulation registers;
 //  * decode (M_pad <= 16): the weight stream dominates (a few tokens against
 //    the whole weight), so each workgroup owns 16 output columns, its waves
 //    split K, every wave issues all of its weight loads before its first MFMA,
@@ -33,19 +33,22 @@ struct Bf16Op {
     __device__ static __forceinline__ Acc mfma(Frag a, Frag b, Acc c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
+    // the same MFMA with the accumulators held in accumulation registers (four-wave engine)
+    __device__ static __forceinline__ void mfma_acc(Acc &c, Frag a, Frag b) {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    }
     __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const {
         u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         st8(out + (int64_t)mrow * n + ncol, p);
     }
 };
 
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
-__global__ void __attribute__((amdgpu_flat_work_group_size(64 * WM * WN, 64 * WM * WN)))
-__attribute__((amdgpu_waves_per_eu((WM * WN + 3) / 4, (WM * WN + 3) / 4)))
-gemm_bf16_prefill_kernel(GemmShape g, uint16_t *out) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (BM + BN) * KT_BYTES + PF_BYTES];
+template <int BN, int PF>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + BN) * KT_BYTES + PF_BYTES];
     Bf16Op op{out, g.n};
-    gemm_nt_persistent<BM, BN, WM, WN, PRIO, PF, SCHED>(g, op, smem);
+    gemm_nt_wide<BN, PF>(g, op, smem);
 }
 
 // ---------------------------------------------------------------- decode path
@@ -98,13 +101,6 @@ gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint1
 }
 
 // ---------------------------------------------------------------- launchers
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED>
-static hipError_t launch_prefill(const GemmShape &g, uint16_t *out, hipStream_t st) {
-    const int nt = ((g.m_pad + BM - 1) / BM) * ((g.n + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_bf16_prefill_kernel<BM, BN, WM, WN, PRIO, PF, SCHED>), dim3(persistent_grid(nt)), dim3(64 * WM * WN), 0, st, g, out);
-    return hipGetLastError();
-}
-
 hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw, uint16_t *out,
                                int m, int m_pad, int n, int k, hipStream_t st) {
     if (m_pad <= 16) {
@@ -114,8 +110,9 @@ hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w
     }
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),
                 ldx * 2, ldw * 2, m, m_pad, n, k * 2, 4};
-    if (pick_tile_n(m_pad, n) == 224) return launch_prefill<256, 224, 4, 2, false, 3, 2>(g, out, st);
-    return launch_prefill<256, 256, 2, 4, true, 3, 3>(g, out, st);
+    const int nt = ((m_pad + 255) / 256) * ((n + 223) / 224);
+    hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
+    return hipGetLastError();
 }
 
 }  // namespace rpl

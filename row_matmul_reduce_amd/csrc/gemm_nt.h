@@ -306,6 +306,197 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
     if (have_prev) store_tile(pm0, pn0);
 }
 
+// Four-wave form of the engine: a 256 x BN tile (BN = 224 or 256) on 2 x 2 waves,
+// 128 x BN/2 outputs per wave.  Per MFMA it reads a third fewer fragments from
+// LDS than the 8-wave form (16 fragment reads feed 64 MFMAs instead of 8 feeding
+// 16), and with one wave per SIMD each wave owns the whole register file: the
+// 128 x 112 (or 128 x 128) fp32 accumulators live in the 256 accumulation
+// registers, pinned there by Op::mfma_acc (an MFMA written as inline assembly on
+// an "a"-constrained operand), which leaves the 256 vector registers to the two
+// fragment sets and the addressing.
+//
+// The step is the same as above (128 bytes of K per row, double-buffered, DMA
+// of step k+2 into the buffer released by step k's barrier, L2 prefetch of step
+// k+PF), but the interleave is explicit rather than requested from the
+// scheduler: each half-step is cut into FM+FN groups of MFMAs, each followed by
+// one fragment read of the other half (and, in the second half, one DMA
+// instruction), with a sched_barrier after every group, so the issue order is
+// exactly that.  Each wave issues 8 + FN DMA instructions per step (activation
+// groups wave, wave+4, ...; weight groups likewise), as many as it reads
+// fragments.  The K loop is unrolled by two so that the buffer addresses are
+// constants.
+//
+// Hazards the compiler cannot see through inline assembly: zeroed accumulators
+// are written before the first MFMA reads them (a tie to each, then s_nop), and
+// the results of the last MFMAs of a tile are read only after enough wait
+// states (an s_nop tied to the accumulators of the last group; every earlier
+// group sits behind a sched_barrier and has long completed).
+// smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS.
+template <int BN, int PF, class Op>
+__device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, uint8_t *smem) {
+    constexpr int BM = 256, NW = 4, WN = 2;
+    constexpr int TM = BM / 2, TN = BN / WN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int GA = BM / 8, GB = BN / 8;            // 8-row (1 KB) groups per operand per step
+    constexpr int NA = GA / NW, NB = GB / NW;          // DMA instructions per wave per step
+    constexpr int NR = FM + FN, NM = FM * FN;          // fragment reads and MFMAs per half-step
+    static_assert(GA % NW == 0 && GB % NW == 0 && NA + NB == NR, "one DMA per fragment read");
+    static_assert(BM / PF_SHARE_X <= 64, "activation prefetch slice fits one wave");
+    constexpr int BUF = (BM + BN) * KT_BYTES;
+    using Frag = typename Op::Frag;
+    using Acc = typename Op::Acc;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
+    const int nt_m = (g.m_pad + BM - 1) / BM, nt_n = (g.n + BN - 1) / BN;
+    const int total = nt_m * nt_n;
+    const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
+    uint8_t *const s0 = smem, *const s1 = smem + BUF, *const sink = smem + 2 * BUF;
+    const int lr = lane >> 3;
+    const int pc = (lane & 7) ^ lr;
+    const int frow = lane & 15, fchunk = lane >> 4;
+    const int pfw_rows = BN / g.group_m;
+
+    __amdgpu_buffer_rsrc_t rx, rw;
+    int pfx0 = 0, pfw0 = 0;  // first row of this workgroup's prefetch slice (activation, weight)
+    // DMA instruction j of step kt into buf: activation group j*NW + wave (j < NA), else
+    // weight group (j-NA)*NW + wave.  j is a compile-time constant at every call.
+    auto dma = [&](int kt, uint8_t *buf, int j) {
+        const int kb = kt * KT_BYTES + pc * 16;
+        const bool kin = kb < g.kbytes;
+        if (j < NA) {
+            const int gi = j * NW + wave;
+            const uint32_t v = kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
+        } else {
+            const int gj = (j - NA) * NW + wave;
+            const uint32_t v = kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
+                                                     0, 0, 0);
+        }
+    };
+    // Shared L2 prefetch as in the 8-wave form: activation slice on wave 0, weight slice
+    // on wave 1, an out-of-range load on the others (the barrier's vmcnt counts on one).
+    auto prefetch = [&](int kt) {
+        const int kb = kt * KT_BYTES;
+        uint32_t v = OOB_OFFSET;
+        if (wave == 0) {
+            if (lane < BM / PF_SHARE_X && kb < g.kbytes) v = (uint32_t)((pfx0 + lane) * g.ldx + kb);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
+        } else {
+            if (wave == 1 && lane < pfw_rows && kb < g.kbytes) v = (uint32_t)((pfw0 + lane) * g.ldw + kb);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)sink, 4, v, 0, 0, 0);
+        }
+    };
+
+    Acc acc[FM][FN];
+    Frag xa[FM], wa[FN], xb[FM], wb[FN];
+    auto frag = [&](const uint8_t *buf, bool isw, int i, int half) -> Frag {
+        const uint8_t *base = isw ? buf + BM * KT_BYTES : buf;
+        const int row = (isw ? wn0 : wm0) + i * 16 + frow;
+        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(base + swz_off(row, half * 4 + fchunk)));
+    };
+    // One half-step: the MFMAs on (x, w) in NR groups; after group q, fragment q of the
+    // other set is read from rbuf (activation fragments first), and in the second half
+    // DMA instruction q of step dma_kt goes into dbuf.
+    auto half = [&](const Frag *x, const Frag *w, Frag *lx, Frag *lw, const uint8_t *rbuf, int rhalf, bool with_dma,
+                    int dma_kt, uint8_t *dbuf) {
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+#pragma unroll
+            for (int i = q * NM / NR; i < (q + 1) * NM / NR; ++i) Op::mfma_acc(acc[i / FN][i % FN], w[i % FN], x[i / FN]);
+            if (q < FM) lx[q] = frag(rbuf, false, q, rhalf);
+            else lw[q - FM] = frag(rbuf, true, q - FM, rhalf);
+            if (with_dma) dma(dma_kt, dbuf, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto landed = [&](const Frag *xf, const Frag *wf) {
+#pragma unroll
+        for (int a = 0; a < FM; ++a) asm volatile("" ::"v"(xf[a]));
+#pragma unroll
+        for (int b = 0; b < FN; ++b) asm volatile("" ::"v"(wf[b]));
+    };
+    auto barrier = [&]() {
+        if (PF > 0) asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Step kt reads buffer cur; step kt+1 lands in nxt; step kt+2's DMA goes into cur once
+    // every wave has passed this step's barrier.
+    auto kstep = [&](int kt, uint8_t *cur, uint8_t *nxt) {
+        if (PF > 0) prefetch(kt + PF);  // past the end: out of range, reads nothing
+        __builtin_amdgcn_sched_barrier(0);
+        half(xa, wa, xb, wb, cur, 1, false, 0, nullptr);
+        landed(xb, wb);
+        barrier();
+        // Unconditional (one basic block): after the last step the reads fetch a buffer
+        // nobody uses and the DMA offsets are out of range (zero fill of this wave's own
+        // groups, ahead of its next tile's DMA into them).
+        half(xb, wb, xa, wa, nxt, 0, true, kt + 2, cur);
+        landed(xa, wa);
+    };
+    // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
+    auto store_tile = [&](int m0, int n0) {
+        constexpr int LAST = (NR - 1) * NM / NR;  // first MFMA of the last group
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
+#pragma unroll
+        for (int i = LAST + 1; i < NM; ++i) asm volatile("" : "+a"(acc[i / FN][i % FN]));
+#pragma unroll
+        for (int a = 0; a < FM; ++a) {
+            const int mrow = m0 + wm0 + a * 16 + frow;
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
+                if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
+            }
+        }
+    };
+
+    int pm0 = 0, pn0 = 0;
+    bool have_prev = false;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        int tm, tn;
+        tile_of_block(t, nt_m, nt_n, g.group_m, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
+        rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
+        pfx0 = (tn % PF_SHARE_X) * (BM / PF_SHARE_X);
+        pfw0 = (tm % g.group_m) * pfw_rows;
+        for (int d = 2; d < PF; ++d) prefetch(d);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) dma(0, s0, j);  // the previous tile's reads all ended at its barriers
+        if (have_prev) store_tile(pm0, pn0);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) dma(1, s1, j);  // out of range (zeros) when ksteps == 1
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                acc[a][b] = Op::zero();
+                asm volatile("" : "+a"(acc[a][b]));
+            }
+        // step 0 and the stores have landed (step 1's NR DMAs may still be in flight);
+        // the s_nop separates the accumulator writes from the first MFMA
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier\n\ts_nop 4" ::"n"(NR) : "memory");
+#pragma unroll
+        for (int a = 0; a < FM; ++a) xa[a] = frag(s0, false, a, 0);
+#pragma unroll
+        for (int b = 0; b < FN; ++b) wa[b] = frag(s0, true, b, 0);
+        landed(xa, wa);
+        for (int kt = 0; kt < ksteps; kt += 2) {
+            kstep(kt, s0, s1);
+            if (kt + 1 < ksteps) kstep(kt + 1, s1, s0);
+        }
+        pm0 = m0;
+        pn0 = n0;
+        have_prev = true;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
+    if (have_prev) store_tile(pm0, pn0);
+}
+
 // Grid of the persistent tile loop.
 __host__ __device__ inline int persistent_grid(int tiles) { return tiles < NUM_CU ? tiles : NUM_CU; }
 
