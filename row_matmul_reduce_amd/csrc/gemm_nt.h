@@ -392,10 +392,15 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
 
     Acc acc[FM][FN];
     Frag xa[FM], wa[FN], xb[FM], wb[FN];
+    // Fragment i of a half is 16 rows below fragment 0 and, as wm0, wn0 and 16 are multiples
+    // of 8, has the same swizzle: one lane offset per operand and half, plus a constant.
+    static_assert(TM % 8 == 0 && TN % 8 == 0, "fragment rows keep the swizzle of the first");
+    const uint32_t fx0 = swz_off(wm0 + frow, fchunk), fx1 = swz_off(wm0 + frow, 4 + fchunk);
+    const uint32_t fw0 = BM * KT_BYTES + swz_off(wn0 + frow, fchunk);
+    const uint32_t fw1 = BM * KT_BYTES + swz_off(wn0 + frow, 4 + fchunk);
     auto frag = [&](const uint8_t *buf, bool isw, int i, int half) -> Frag {
-        const uint8_t *base = isw ? buf + BM * KT_BYTES : buf;
-        const int row = (isw ? wn0 : wm0) + i * 16 + frow;
-        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(base + swz_off(row, half * 4 + fchunk)));
+        const uint32_t off = isw ? (half ? fw1 : fw0) : (half ? fx1 : fx0);
+        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(buf + off + i * 16 * KT_BYTES));
     };
     // One half-step: the MFMAs on (x, w) in NR groups; after group q, fragment q of the
     // other set is read from rbuf (activation fragments first), and in the second half
