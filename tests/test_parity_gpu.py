@@ -47,13 +47,14 @@ SMALL_SHAPES = [
     (3, 40, 64, 4),        # decode kernel, ragged column tile
     (16, 264, 2048, 2),    # decode kernel at m_pad = 16, K split over every wave
     (8, 3584, 3584, 2),    # decode o_proj shape
-    (17, 64, 128, 8),      # tile kernel with bounds checks, m_pad = 24
+    (17, 64, 128, 8),      # tile kernel with bounds checks, m_pad = 24, a single K step
     (300, 520, 656, 2),    # ragged m, n and K (k_shard = 328)
     (257, 264, 288, 4),    # m_pad = 260: one row past a 256-row tile
     (512, 448, 256, 2),    # whole 256 x 224 tiles (no bounds checks)
-    (512, 512, 512, 4),    # whole 256 x 256 tiles (no bounds checks)
-    (4100, 4104, 272, 2),  # 289 tiles of 256 x 256 > 256 workgroups: some run two tiles; ragged m, n, K
-    (8192, 3584, 128, 2),  # 512 tiles of 256 x 224: every workgroup runs two tiles
+    (512, 512, 512, 4),    # 2 x 3 tiles of 256 x 224, the last tile column 64 wide
+    (4100, 4104, 272, 2),  # 17 x 19 = 323 tiles > 256 workgroups: some run two; ragged m, n, K; 3 K steps
+    (8192, 3584, 128, 2),  # 512 tiles of 256 x 224: every workgroup runs two tiles of one K step
+    (4100, 4480, 256, 2),  # 17 x 20 = 340 tiles, some workgroups run two; 2 K steps per tile
 ]
 
 
