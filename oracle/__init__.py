@@ -92,6 +92,10 @@ def load(path: str):
     L.orc_quant_per_token.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p]
     L.orc_num_threads.restype = ctypes.c_int
     L.orc_set_num_threads.argtypes = [ctypes.c_int]
+    L.orc_shard_rows.argtypes = [_p, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _p]
+    L.orc_shard_rows.restype = ctypes.c_int
+    L.orc_gather_rows.argtypes = [_p, ctypes.c_int, _i64, _i64, _i64, _i64, _p]
+    L.orc_gather_rows.restype = ctypes.c_int
     return L
 
 
@@ -317,3 +321,29 @@ def rmsnorm_slice_apply(h, sumsq_parts, n_total: int, gamma_slice, eps: float, w
     if rc != 0:
         raise RuntimeError(f"orc_rmsnorm_slice_apply failed: {rc}")
     return (y, yf) if want_f64 else y
+
+
+def shard_rows(x: np.ndarray, tp: int, rank: int) -> np.ndarray:
+    """Rank `rank`'s token chunk of the zero-padded rows of x ([FC1] pad/shard helpers)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    m, n = x.shape
+    mc = -(-m // tp)
+    out = np.empty((mc, n), dtype=np.uint16)
+    rc = lib().orc_shard_rows(_ptr(x), n, m, n, tp, rank, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"orc_shard_rows failed: {rc}")
+    return out
+
+
+def gather_rows(chunks, m: int) -> np.ndarray:
+    """The tp chunks in rank order, cut back to the first m rows ([FC1] gather + unpad)."""
+    parts = [np.ascontiguousarray(c, dtype=np.uint16) for c in chunks]
+    mc, n = parts[0].shape
+    if any(p.shape != (mc, n) for p in parts):
+        raise ValueError("chunks disagree in shape")
+    out = np.empty((m, n), dtype=np.uint16)
+    arr = _ptr_array(parts)
+    rc = lib().orc_gather_rows(ctypes.cast(arr, _p), len(parts), mc, n, m, n, _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"orc_gather_rows failed: {rc}")
+    return out

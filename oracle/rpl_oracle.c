@@ -42,7 +42,9 @@
  *       clamped to [-127, 127]; an all-zero row has scale 0 and codes 0;
  *   R7  the 910C layout splits the hidden dimension over ranks: each rank
  *       reduces a column slice of every row and contributes the slice's sum of
- *       squares; the full-row sum is their cross-rank sum.
+ *       squares; the full-row sum is their cross-rank sum;
+ *   R8  FC1 pad rows are zero and sit after the M real rows; the gathered
+ *       chunks are cut back to their first M rows.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  * OpenMP only splits independent output rows across threads; every dot
@@ -387,6 +389,44 @@ int orc_quant_per_token(const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
             }
             xq[r * ldq + kk] = q;
         }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------- token rows around the exchange
+ * [FC1] review thread, sequence pad/shard helpers: the M token rows are padded
+ * with rows at the end to M_pad = tp * M_c, M_c = ceil(M / tp); rank r keeps the
+ * contiguous block of padded rows starting at r * M_c; after the layer every
+ * rank's block is gathered in rank order and the gathered rows are cut back to
+ * the first M.  Reading R8: the pad rows are zero (they stand for tokens that
+ * do not exist), and the cut keeps rows 0 .. M-1 of the gathered rows.
+ *   shard:  out[i, :] = x[r * M_c + i, :]  if r * M_c + i < M,  else 0
+ *   gather: out[i, :] = chunk[i / M_c][i mod M_c, :]            for i < M
+ * Both only move bf16 bit patterns.                                          */
+int orc_shard_rows(const uint16_t *x, int64_t ldx, int64_t m, int64_t n, int tp, int rank,
+                   uint16_t *out)
+{
+    if (tp < 1 || rank < 0 || rank >= tp || m < 0 || n < 0 || ldx < n) return ORC_ERR_ARG;
+    const int64_t mc = (m + tp - 1) / tp;
+    if (mc > 0 && (!out || (m > 0 && !x))) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < mc; ++i) {
+        const int64_t src = (int64_t)rank * mc + i;  /* row of the padded rows */
+        for (int64_t j = 0; j < n; ++j)
+            out[i * n + j] = src < m ? x[src * ldx + j] : (uint16_t)0;
+    }
+    return ORC_OK;
+}
+
+int orc_gather_rows(const uint16_t *const *chunks, int tp, int64_t m_chunk, int64_t ld,
+                    int64_t m, int64_t n, uint16_t *out)
+{
+    if (!chunks || tp < 1 || m_chunk < 0 || m < 0 || m > (int64_t)tp * m_chunk || n < 0 || ld < n)
+        return ORC_ERR_ARG;
+    if (m > 0 && !out) return ORC_ERR_ARG;
+    for (int64_t i = 0; i < m; ++i) {
+        const int64_t c = i / m_chunk, r = i % m_chunk;  /* rank c's row r */
+        if (!chunks[c]) return ORC_ERR_ARG;
+        for (int64_t j = 0; j < n; ++j) out[i * n + j] = chunks[c][r * ld + j];
     }
     return ORC_OK;
 }

@@ -446,6 +446,31 @@ def check_quant_properties(orc):
 
 
 # ----------------------------------------------------------------------- golden
+def check_token_rows(orc):
+    """[FC1] pad/shard and gather/unpad: the hand-worked blocks, then properties that hold for any
+    shape -- the gathered blocks give back x exactly, the blocks past the last real row are zero,
+    and with one rank the block is x itself."""
+    with open(GOLDEN) as f:
+        g = json.load(f)["token_rows"]
+    for c in g["cases"]:
+        x = _bits(c["x"])
+        blocks = [orc.shard_rows(x, c["tp"], r) for r in range(c["tp"])]
+        for r, b in enumerate(blocks):
+            assert np.array_equal(b, _bits(c["chunks"][r])), (c["m"], c["tp"], r)
+        assert np.array_equal(orc.gather_rows(blocks, c["m"]), x)
+    rng = np.random.default_rng(91)
+    for m, n, tp in [(1, 8, 1), (9, 16, 1), (9, 16, 2), (13, 8, 4), (29, 24, 8), (64, 8, 8), (3, 8, 8)]:
+        x = rng.integers(1, 0x7F80, (m, n), dtype=np.uint16)  # nonzero finite bf16 patterns
+        blocks = [orc.shard_rows(x, tp, r) for r in range(tp)]
+        mc = -(-m // tp)
+        assert all(b.shape == (mc, n) for b in blocks)
+        assert np.array_equal(orc.gather_rows(blocks, m), x), (m, n, tp)
+        stacked = np.concatenate(blocks, axis=0)
+        assert np.all(stacked[m:] == 0) and np.all(stacked[:m] != 0), (m, n, tp)
+        if tp == 1:
+            assert np.array_equal(blocks[0], x)
+
+
 def check_golden(orc):
     with open(GOLDEN) as f:
         g = json.load(f)
@@ -483,5 +508,5 @@ ALL_CHECKS = [
     check_reduce_bruteforce, check_rms_invariant, check_unit_rms_and_scale_invariance,
     check_zero_row_and_tp1, check_integer_partials_exact, check_w8a8, check_w8a8_overflow,
     check_sum_partials, check_hidden_split_epilogue, check_quant_exact, check_quant_properties,
-    check_golden,
+    check_golden, check_token_rows,
 ]

@@ -7,7 +7,8 @@ residual, a reordered dequantisation, a quantiser that rounds ties away from
 zero, truncates, divides by 128, drops the absolute value or the last column,
 or gives a zero row scale 1; an all-reduce sum that drops a shard; a
 hidden-split epilogue that sums h instead of h^2, averages over the slice or
-drops a rank), compiles each copy with gcc and checks that at
+drops a rank; token blocks at the wrong stride, pad rows that repeat the last
+row, blocks gathered in reverse rank order), compiles each copy with gcc and checks that at
 least one pin fails for every one of them.
 """
 import os
@@ -84,6 +85,15 @@ MUTANTS = [
     ("quant_zero_row_scale_one", "volatile float s = amax / 127.0f;",
      "volatile float s = amax > 0.0f ? amax / 127.0f : 1.0f;"),
     ("quant_truncates", "float v = nearbyintf(t);", "float v = truncf(t);"),
+    ("shard_block_stride_m_over_tp",
+     "const int64_t src = (int64_t)rank * mc + i;",
+     "const int64_t src = (int64_t)rank * (m / tp) + i;"),
+    ("shard_pad_rows_repeat_last_row",
+     "out[i * n + j] = src < m ? x[src * ldx + j] : (uint16_t)0;",
+     "out[i * n + j] = x[(src < m ? src : m - 1) * ldx + j];"),
+    ("gather_blocks_in_reverse_rank_order",
+     "const int64_t c = i / m_chunk, r = i % m_chunk;",
+     "const int64_t c = tp - 1 - i / m_chunk, r = i % m_chunk;"),
     ("w8a8_sign_of_weight",
      "s += (int64_t)xr[kk] * (int64_t)wr[kk];",
      "s += (int64_t)xr[kk] * (int64_t)(kk == 0 ? -wr[kk] : wr[kk]);"),
