@@ -19,8 +19,8 @@ so each precision is its own path.  The default run times the bf16 prefill down_
 the w8a8 twin, the decode o_proj share and the TP=8 long-prefill share as side
 steps (w8a8 both from int8 inputs and from the bf16 activation), plus the
 single-launch decode path (every shard's product + sum + residual + RMSNorm in one
-kernel) for a token chunk and for all rows, the all-reduce sum and the hidden-split
-epilogue.  Every step cycles through several copies of its inputs (more than
+kernel) for a token chunk and for all rows, the all-reduce sum, the hidden-split
+epilogue and the token-row shard/gather around the exchange.  Every step cycles through several copies of its inputs (more than
 twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "quant_per_token": ["quant_per_token.hip", "rpl_device.h"],
     "decode_fused": ["decode_fused.hip", "rpl_device.h"],
     "reduce_variants": ["reduce_variants.hip", "rpl_device.h"],
+    "token_rows": ["token_rows.hip", "rpl_device.h"],
 }
 # kernels that live in a shared source file
 KERNEL_KEY = {"sum_partials": "reduce_variants", "slice_sumsq": "reduce_variants", "slice_apply": "reduce_variants"}
@@ -371,6 +372,37 @@ def reduce_variants(torch, rpl, copies: int):
     return out
 
 
+def token_rows(torch, rpl, copies: int):
+    """The FlashComm1 token-row movement on the TP=8 long-prefill rows, HBM-resident: rank 0's block
+    of the padded residual rows (16384 x 5120 -> 2048 x 5120) and the gather of the 8 ranks' blocks
+    back to all 16384 rows."""
+    from row_matmul_reduce_amd import synth
+    rng = np.random.default_rng(1)
+
+    def bf(shape):
+        return torch.from_numpy(synth.bf16_bits(rng.standard_normal(shape, dtype=np.float32)).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    wl = synth.WORKLOADS[WORKLOAD_IDS["long_prefill"]]
+    m, n, tp, mc = wl.m, wl.n, wl.tp, wl.m_chunk
+    base = [bf((mc, n)) for _ in range(tp)]
+    nb = 2 * tp * mc * n * 2  # blocks read + rows written per gather
+    k = copies if copies > 0 else max(2, -(-(2 * MALL_BYTES + 1) // nb) + 1)
+    sets = [base] + [[t.clone() for t in base] for _ in range(k - 1)]
+    rows = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    us_g = _graph_mean_us(torch, lambda i: rpl.rpl_gather_rows(sets[i % len(sets)], m, out=rows), len(sets))
+    del sets, base
+    xs = [bf((m, n)) for _ in range(max(2, -(-(2 * MALL_BYTES + 1) // (m * n * 2)) + 1))]
+    blk = torch.empty((mc, n), dtype=torch.bfloat16, device="cuda")
+    us_s = _graph_mean_us(torch, lambda i: rpl.rpl_shard_rows(xs[i % len(xs)], tp, 0, out=blk), len(xs))
+    bg, bs = 2 * m * n * 2, 2 * mc * n * 2
+    return {"token_rows": {"workload": wl.name, "rows": m, "cols": n, "ranks": tp,
+                           "gather_us": us_g, "gather_bytes": bg, "gather_GB/s": bg / (us_g * 1e-6) / 1e9,
+                           "gather_frac_hbm": bg / (us_g * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                           "shard_us": us_s, "shard_bytes": bs, "shard_GB/s": bs / (us_s * 1e-6) / 1e9,
+                           "shard_frac_hbm": bs / (us_s * 1e-6) / 1e9 / PEAK_HBM_GBS}}
+
+
 def library_reference(path, torch, steps: int):
     """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
     HBM-resident input sets, same stream and timing method, to show what the chip gives under the
@@ -504,6 +536,8 @@ def main():
             side[key] = fused_decode(torch, rpl, args.copies, all_rows)
             torch.cuda.empty_cache()
         side.update(reduce_variants(torch, rpl, args.copies))
+        torch.cuda.empty_cache()
+        side.update(token_rows(torch, rpl, args.copies))
         torch.cuda.empty_cache()
 
     cpu = None

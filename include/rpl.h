@@ -12,7 +12,11 @@
  *                             (what a reduce-scatter delivers), residual add,
  *                             RMSNorm;
  *   rpl_w8a8_partial          the int8 x int8 (w8a8 dynamic-quant) variant of
- *                             the partial, dequantised to bf16.
+ *                             the partial, dequantised to bf16;
+ *
+ * and around them the per-token quantiser, the single-launch decode path, the
+ * all-reduce and hidden-split forms of the reduction, and the token-row
+ * shard/gather of the FlashComm1 layout.
  *
  * Sources (web pages; cited by title and section):
  *   [FC1]  xLLM pull request #1890, "feat: add FlashComm1 and MMRS fusion support
@@ -328,10 +332,45 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
                                      void *workspace, int64_t workspace_bytes,
                                      void *stream);
 
+/*
+ * rpl_shard_rows / rpl_gather_rows -- the token-row movement around the
+ * exchange in the FlashComm1 layout.
+ *
+ * [FC1] review thread (sequence pad/shard helpers): the M token rows are padded
+ * at the end to M_pad = tp * M_c rows, M_c = ceil(M / tp); rank r keeps the
+ * block of padded rows starting at r * M_c; after the layer all ranks' blocks
+ * are gathered in rank order and cut back to the first M rows.  Pad rows are
+ * zero.
+ *
+ * rpl_shard_rows:   out[i, :] = x[rank * M_c + i, :] if rank * M_c + i < m, else 0
+ *   x    [m, n] bf16, row stride ldx >= n
+ *   out  [M_c, n] bf16 contiguous, must not overlap x
+ *   The rank's block is written in one pass, with no padded copy of x.
+ *
+ * rpl_gather_rows:  out[i, :] = chunks[i / m_chunk][i % m_chunk, :]   for i < m
+ *   chunks  HOST array of tp DEVICE pointers, each -> [m_chunk, n] bf16 with
+ *           row stride ld (on one GPU every rank's block is given directly)
+ *   out     [m, n] bf16 contiguous, m <= tp * m_chunk (rows past m are the pad
+ *           rows and are dropped); must not overlap a block
+ *
+ * RPL_ERR_NULL        shard: m > 0 and x or out is NULL; gather: chunks is
+ *                     NULL, or m > 0 and out or a chunks[s] is NULL
+ * RPL_ERR_INVALID     m < 0, n < 1, tp < 1, shard: rank outside [0, tp);
+ *                     gather: m_chunk < 0 or m > tp * m_chunk; ld < n; overlaps
+ * RPL_ERR_UNSUPPORTED n or the row stride not a multiple of 8; pointers not
+ *                     16-byte aligned; gather: tp > RPL_MAX_TP; sizes >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed
+ */
+rpl_status rpl_shard_rows(const rpl_bf16 *x, int64_t ldx, int64_t m, int64_t n, int32_t tp,
+                          int32_t rank, rpl_bf16 *out, void *stream);
+
+rpl_status rpl_gather_rows(const rpl_bf16 *const *chunks, int32_t tp, int64_t m_chunk, int64_t ld,
+                           int64_t m, int64_t n, rpl_bf16 *out, void *stream);
+
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 1.3. */
+/* Library ABI version: (major << 16) | minor.  Currently 1.4. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

@@ -18,6 +18,8 @@ the library is missing, every call raises.
     rpl_sum_partials(partials)                 -> bf16 sum (all-reduce form)
     rpl_reduce_slice_sumsq / rpl_rmsnorm_slice_apply
                                                hidden-split epilogue, two steps
+    rpl_shard_rows(x, tp, rank)                -> the rank's block of the padded rows
+    rpl_gather_rows(chunks, m)                 -> blocks in rank order, pad rows dropped
 """
 from __future__ import annotations
 
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.rpl_rmsnorm_slice_apply.argtypes = [_p, _p, _i32, _i64, _i64, _i64, _p, ctypes.c_float, _p, _i64, _p]
         L.rpl_quant_per_token.restype = ctypes.c_int
         L.rpl_quant_per_token.argtypes = [_p, _i64, _p, _i64, _p, _i64, _i64, _p]
+        L.rpl_shard_rows.restype = ctypes.c_int
+        L.rpl_shard_rows.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, _p, _p]
+        L.rpl_gather_rows.restype = ctypes.c_int
+        L.rpl_gather_rows.argtypes = [_p, _i32, _i64, _i64, _i64, _i64, _p, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
         L.rpl_status_string.argtypes = [ctypes.c_int]
         L.rpl_version.restype = ctypes.c_int32
@@ -257,6 +263,42 @@ def rpl_sum_partials(partials, out=None, stream=None):
     keep, arr = _ptrs(partials)
     st = lib().rpl_sum_partials(arr, len(partials), m, n, ldp, out.data_ptr(), _stream(out, stream))
     _check("rpl_sum_partials", st)
+    return out
+
+
+def rpl_shard_rows(x, tp: int, rank: int, out=None, stream=None):
+    """Rank `rank`'s block of the zero-padded token rows of x [m, n]: [ceil(m/tp), n]."""
+    torch = _torch()
+    _dev(x, "x", torch.bfloat16, 2)
+    m, n = x.shape
+    mc = -(-m // tp) if tp >= 1 else 0
+    if out is None:
+        out = torch.empty((mc, n), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (mc, n) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{mc}, {n}] tensor")
+    st = lib().rpl_shard_rows(x.data_ptr(), _ld(x), m, n, tp, rank, out.data_ptr(), _stream(out, stream))
+    _check("rpl_shard_rows", st)
+    return out
+
+
+def rpl_gather_rows(chunks, m: int, out=None, stream=None):
+    """The tp [m_chunk, n] blocks in rank order, cut back to the first m rows: [m, n]."""
+    torch = _torch()
+    for i, t in enumerate(chunks):
+        _dev(t, f"chunks[{i}]", torch.bfloat16, 2)
+    mc, n = chunks[0].shape
+    ld = _ld(chunks[0])
+    if any(t.shape != (mc, n) or _ld(t) != ld for t in chunks):
+        raise ValueError("chunks must share shape and row stride")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=chunks[0].device)
+    _dev(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (m, n) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{m}, {n}] tensor")
+    keep, arr = _ptrs(chunks)
+    st = lib().rpl_gather_rows(arr, len(chunks), mc, ld, m, n, out.data_ptr(), _stream(out, stream))
+    _check("rpl_gather_rows", st)
     return out
 
 

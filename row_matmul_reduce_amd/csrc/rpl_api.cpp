@@ -155,6 +155,44 @@ rpl_status rpl_sum_partials(const rpl_bf16 *const *partials, int32_t tp, int64_t
     return launch_status(rpl::launch_sum_partials(p, tp, (int)m, (int)n, ldp, out, static_cast<hipStream_t>(stream)));
 }
 
+rpl_status rpl_shard_rows(const rpl_bf16 *x, int64_t ldx, int64_t m, int64_t n, int32_t tp, int32_t rank,
+                          rpl_bf16 *out, void *stream) {
+    if (m > 0 && (!x || !out)) return RPL_ERR_NULL;
+    if (m < 0 || n < 1 || tp < 1 || rank < 0 || rank >= tp || ldx < n) return RPL_ERR_INVALID;
+    const int64_t mc = (m + tp - 1) / tp;
+    if (m > 0 && overlap(out, span(mc, n, n, 2), x, span(m, n, ldx, 2))) return RPL_ERR_INVALID;
+    if (n % 8 || ldx % 8 || !aligned(x, 16) || !aligned(out, 16)) return RPL_ERR_UNSUPPORTED;
+    if (m > kMaxDim || n > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    return launch_status(rpl::launch_shard_rows(x, ldx, (int)m, (int)n, tp, rank, out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_gather_rows(const rpl_bf16 *const *chunks, int32_t tp, int64_t m_chunk, int64_t ld, int64_t m,
+                           int64_t n, rpl_bf16 *out, void *stream) {
+    if (!chunks) return RPL_ERR_NULL;
+    if (m > 0) {
+        if (!out) return RPL_ERR_NULL;
+        if (tp >= 1 && tp <= RPL_MAX_TP)
+            for (int s = 0; s < tp; ++s)
+                if (!chunks[s]) return RPL_ERR_NULL;
+    }
+    if (tp < 1 || m_chunk < 0 || m < 0 || n < 1 || ld < n || m > (int64_t)tp * m_chunk) return RPL_ERR_INVALID;
+    const int np = tp <= RPL_MAX_TP ? tp : 0;
+    const int64_t ob = span(m, n, n, 2), cb = span(m_chunk, n, ld, 2);
+    for (int s = 0; s < np && m > 0; ++s)
+        if (overlap(out, ob, chunks[s], cb)) return RPL_ERR_INVALID;
+    if (tp > RPL_MAX_TP || n % 8 || ld % 8 || (m > 0 && !aligned(out, 16))) return RPL_ERR_UNSUPPORTED;
+    for (int s = 0; s < tp && m > 0; ++s)
+        if (!aligned(chunks[s], 16)) return RPL_ERR_UNSUPPORTED;
+    if (m_chunk > kMaxDim || n > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (m == 0) return RPL_OK;
+    rpl::PartialPtrs p{};
+    for (int s = 0; s < tp; ++s) p.p[s] = chunks[s];
+    return launch_status(rpl::launch_gather_rows(p, (int)m_chunk, ld, (int)m, (int)n, out,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 rpl_status rpl_reduce_slice_sumsq(const rpl_bf16 *const *partials, int32_t tp, int64_t m, int64_t n_slice,
                                   int64_t ld, const rpl_bf16 *residual, rpl_bf16 *residual_out, float *h_out,
                                   float *sumsq, void *stream) {
@@ -319,6 +357,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (1 << 16) | 3; }
+int32_t rpl_version(void) { return (1 << 16) | 4; }
 
 }  // extern "C"

@@ -48,6 +48,10 @@ hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st);
 
 hipError_t launch_sum_partials(const PartialPtrs &p, int tp, int m, int n, int64_t ldp, uint16_t *out,
                                hipStream_t st);
+hipError_t launch_shard_rows(const uint16_t *x, int64_t ldx, int m, int n, int tp, int rank, uint16_t *out,
+                             hipStream_t st);
+hipError_t launch_gather_rows(const PartialPtrs &chunks, int m_chunk, int64_t ld, int m, int n, uint16_t *out,
+                              hipStream_t st);
 hipError_t launch_slice_sumsq(const PartialPtrs &p, int tp, int m, int ns, int64_t ld, const uint16_t *residual,
                               uint16_t *residual_out, float *h, float *sumsq, hipStream_t st);
 hipError_t launch_slice_apply(const float *h, const SumsqPtrs &s, int tp, int m, int ns, int n_total,

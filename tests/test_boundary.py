@@ -33,7 +33,7 @@ def test_header_declares_the_path_calls():
     for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
               "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace_size",
               "rpl_sum_partials", "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
-              "rpl_status_string", "rpl_version"):
+              "rpl_shard_rows", "rpl_gather_rows", "rpl_status_string", "rpl_version"):
         assert f in names
 
 
@@ -52,7 +52,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (1 << 16) | 3
+    assert rpl.rpl_version() == (1 << 16) | 4
 
 
 class Buf:
@@ -307,6 +307,40 @@ def test_sum_partials_validation():
     for b in (P0, P1, O):
         assert b.untouched()
     assert call([None, None], tp, 0, n, n, None) == OK
+
+
+def test_token_rows_validation():
+    L = rpl.lib()
+    m, n, tp = 5, 64, 2
+    mc = 3
+    X, O = Buf(m * n * 2), Buf(mc * n * 2)
+    x, o = X.ptr, O.ptr
+    shard = lambda x_, ld, m_, n_, tp_, r, out: L.rpl_shard_rows(x_, ld, m_, n_, tp_, r, out, None)
+    cases = [((None, n, m, n, tp, 0, o), NULL), ((x, n, m, n, tp, 0, None), NULL),
+             ((x, n, -1, n, tp, 0, o), INVALID), ((x, n, m, 0, tp, 0, o), INVALID), ((x, n, m, n, 0, 0, o), INVALID),
+             ((x, n, m, n, tp, 2, o), INVALID), ((x, n, m, n, tp, -1, o), INVALID), ((x, 56, m, n, tp, 0, o), INVALID),
+             ((x, n, m, n, tp, 0, x + 64), INVALID),
+             ((x, 60, m, 60, tp, 0, o), UNSUP), ((x, 68, m, n, tp, 0, o), UNSUP), ((x + 8, n, m, n, tp, 0, o), UNSUP),
+             ((x, n, m, n, tp, 0, o + 8), UNSUP)]
+    for args, want in cases:
+        assert shard(*args) == want, args
+    assert shard(None, n, 0, n, tp, 1, None) == OK
+    C0, C1, G = Buf(mc * n * 2), Buf(mc * n * 2), Buf(m * n * 2)
+    c, g = [C0.ptr, C1.ptr], G.ptr
+    gather = lambda cs, tp_, mc_, ld, m_, n_, out: L.rpl_gather_rows(_parr(cs) if cs is not None else None, tp_, mc_,
+                                                                    ld, m_, n_, out, None)
+    cases = [((None, tp, mc, n, m, n, g), NULL), (([C0.ptr, None], tp, mc, n, m, n, g), NULL),
+             ((c, tp, mc, n, m, n, None), NULL),
+             ((c, 0, mc, n, m, n, g), INVALID), ((c, tp, -1, n, m, n, g), INVALID), ((c, tp, mc, n, -1, n, g), INVALID),
+             ((c, tp, mc, n, 7, n, g), INVALID), ((c, tp, mc, n, m, 0, g), INVALID), ((c, tp, mc, 56, m, n, g), INVALID),
+             ((c, tp, mc, n, m, n, C1.ptr + 32), INVALID),
+             ((c * 9, 17, mc, n, m, n, g), UNSUP), ((c, tp, mc, 68, m, n, g), UNSUP), ((c, tp, mc, 60, m, 60, g), UNSUP),
+             ((c, tp, mc, n, m, n, g + 8), UNSUP), (([C0.ptr + 8, C1.ptr], tp, mc, n, m, n, g), UNSUP)]
+    for args, want in cases:
+        assert gather(*args) == want, args
+    for b in (X, O, C0, C1, G):
+        assert b.untouched()
+    assert gather([None, None], tp, mc, n, 0, n, None) == OK
 
 
 def test_hidden_split_validation():
