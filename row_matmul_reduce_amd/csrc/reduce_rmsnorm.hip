@@ -14,8 +14,8 @@
 //   y            = bf16( gamma * h * rsqrt(mean(h^2) + eps) )
 //
 // HBM-bound: every byte is read or written once.  A row is owned by a team of
-// RW wavefronts; lane t of the team holds 16-byte chunks t, t + 64*RW, ... of
-// the row (CPL of them) in fp32 registers, so the row is read once, the sum of
+// RW wavefronts (ROWS rows per workgroup); lane t of the team holds 16-byte
+// chunks t, t + 64*RW, ... of the row (CPL of them) in fp32 registers, so the row is read once, the sum of
 // squares is a wavefront butterfly (plus an LDS exchange between the team's
 // waves when RW > 1), and both outputs are written from registers.  All loads
 // of a group of G partials (and the residual and gamma up front) are issued
@@ -33,13 +33,12 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int CPL, int RW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
+template <int CPL, int RW, int ROWS>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * RW * ROWS, 64 * RW * ROWS)))
 reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t *__restrict__ residual,
                       const uint16_t *__restrict__ gamma, float eps, uint16_t *y, uint16_t *residual_out) {
-    constexpr int ROWS = 4 / RW;            // rows per 256-thread workgroup
     constexpr int G = CPL <= 4 ? 4 : 2;     // partials whose loads are in flight together
-    __shared__ float team_sum[4];
+    __shared__ float team_sum[RW * ROWS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * ROWS + wave / RW;
     const int t = (wave % RW) * 64 + lane;
@@ -120,36 +119,31 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
     }
 }
 
-template <int CPL, int RW>
+template <int CPL, int RW, int ROWS = 4 / RW>
 static hipError_t launch_rr(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
                             const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
-    constexpr int ROWS = 4 / RW;
-    hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPL, RW>), dim3((m_chunk + ROWS - 1) / ROWS), dim3(256), 0, st, p, tp,
-                       m_chunk, n, residual, gamma, eps, y, ro);
+    hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPL, RW, ROWS>), dim3((m_chunk + ROWS - 1) / ROWS),
+                       dim3(64 * RW * ROWS), 0, st, p, tp, m_chunk, n, residual, gamma, eps, y, ro);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
                                  const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
-    // The fewest wavefronts per row that keep each lane at <= 4 chunks (32 values),
-    // or 4 wavefronts with up to 8 chunks for the widest rows (n <= 16384).
+    // Few rows (decode steps): the kernel is one memory round trip long, so each row is
+    // spread over 8 wavefronts (1-4 chunks per lane).  Many rows: one wavefront per row
+    // (up to 8 chunks per lane, no cross-wave exchange), or 4 per row for rows wider than
+    // 4096.  Measured on MI355X: decode chunk 3.8 -> 2.4 us, prefill chunk 15.1 -> 13.1 us.
     const int nch = n / 8;
-    if (nch <= 64 * 4) {
-        switch ((nch + 63) / 64) {
 #define RR(C, W) \
-    case C: return launch_rr<C, W>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
-            RR(1, 1) RR(2, 1) RR(3, 1) RR(4, 1)
-        }
-    } else if (nch <= 128 * 4) {
-        switch ((nch + 127) / 128) {
-            RR(3, 2) RR(4, 2)
-        }
+    case C: return launch_rr<C, W, 1>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
+    if (m_chunk < 512) {
+        switch ((nch + 511) / 512) { RR(1, 8) RR(2, 8) RR(3, 8) RR(4, 8) }
+    } else if (nch <= 64 * 8) {
+        switch ((nch + 63) / 64) { RR(1, 1) RR(2, 1) RR(3, 1) RR(4, 1) RR(5, 1) RR(6, 1) RR(7, 1) RR(8, 1) }
     } else {
-        switch ((nch + 255) / 256) {
-            RR(3, 4) RR(4, 4) RR(5, 4) RR(6, 4) RR(7, 4) RR(8, 4)
-#undef RR
-        }
+        switch ((nch + 255) / 256) { RR(3, 4) RR(4, 4) RR(5, 4) RR(6, 4) RR(7, 4) RR(8, 4) }
     }
+#undef RR
     return hipErrorInvalidValue;
 }
 

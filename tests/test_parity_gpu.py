@@ -127,8 +127,11 @@ def test_empty_batch():
 
 
 # ---------------------------------------------------------------------- reduce
+# (tp, m_chunk, n): up to 511 rows each row is spread over 8 waves (1-4 chunks per lane); from 512
+# rows one wave per row (1-8 chunks per lane) or, above 4096 columns, 4 waves per row
 REDUCE_SHAPES = [(1, 3, 8), (2, 5, 64), (3, 7, 3584), (8, 33, 5120), (16, 2, 8192), (2, 4, 8200),
-                 (4, 3, 16384), (2, 1, 520), (8, 130, 1024)]
+                 (4, 3, 16384), (2, 1, 520), (8, 130, 1024), (2, 511, 3584),
+                 (2, 512, 64), (3, 600, 1032), (2, 517, 2056), (2, 520, 4096), (4, 700, 4104), (2, 513, 16384)]
 
 
 @pytest.mark.parametrize("tp,mc,n", REDUCE_SHAPES)
