@@ -106,12 +106,11 @@ __device__ __forceinline__ void quant_chunks(const u32x4 *v, const RowDiv &d, u3
     }
 }
 
-template <int CPL, int RW>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
+template <int CPL, int RW, int ROWS>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64 * RW * ROWS, 64 * RW * ROWS)))
 quant_rows_kernel(const uint16_t *__restrict__ x, int64_t ldx, int8_t *__restrict__ xq, int64_t ldq,
                   float *__restrict__ scale, int m, int k) {
-    constexpr int ROWS = 4 / RW;
-    __shared__ float team_max[4];
+    __shared__ float team_max[RW * ROWS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = blockIdx.x * ROWS + wave / RW;
     const int t = (wave % RW) * 64 + lane;
@@ -196,39 +195,39 @@ quant_rows_long_kernel(const uint16_t *__restrict__ x, int64_t ldx, int8_t *__re
     if (threadIdx.x == 0) scale[row] = d.scale;
 }
 
-template <int CPL, int RW>
+template <int CPL, int RW, int ROWS = 4 / RW>
 static hipError_t launch_q(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq, float *scale, int m, int k,
                            hipStream_t st) {
-    constexpr int ROWS = 4 / RW;
-    hipLaunchKernelGGL((quant_rows_kernel<CPL, RW>), dim3((m + ROWS - 1) / ROWS), dim3(256), 0, st, x, ldx, xq, ldq,
-                       scale, m, k);
+    hipLaunchKernelGGL((quant_rows_kernel<CPL, RW, ROWS>), dim3((m + ROWS - 1) / ROWS), dim3(64 * RW * ROWS), 0, st,
+                       x, ldx, xq, ldq, scale, m, k);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_per_token(const uint16_t *x, int64_t ldx, int8_t *xq, int64_t ldq, float *scale, int m,
                                   int k, hipStream_t st) {
-    // The fewest wavefronts per row that keep each lane at <= 4 chunks, or 4
-    // wavefronts with up to 8 chunks; longer rows take the two-pass kernel.
+    // Few rows (decode steps): each row over 4 wavefronts, one row per workgroup, so the
+    // rows spread over the CUs (8 rows of 1792: 2.6 -> 2.3 us).  Many rows: the fewest
+    // wavefronts per row that keep each lane at <= 4 chunks, or 4 wavefronts with up to
+    // 8 chunks; longer rows take the two-pass kernel.
     const int nch = k / 8;
-    if (nch <= 64 * 4) {
-        switch ((nch + 63) / 64) {
 #define QQ(C, W) \
     case C: return launch_q<C, W>(x, ldx, xq, ldq, scale, m, k, st);
-            QQ(1, 1) QQ(2, 1) QQ(3, 1) QQ(4, 1)
-        }
+#define QL(C) \
+    case C: return launch_q<C, 4, 1>(x, ldx, xq, ldq, scale, m, k, st);
+    if (m < 512 && nch <= 256 * 8) {
+        switch ((nch + 255) / 256) { QL(1) QL(2) QL(3) QL(4) QL(5) QL(6) QL(7) QL(8) }
+    } else if (nch <= 64 * 4) {
+        switch ((nch + 63) / 64) { QQ(1, 1) QQ(2, 1) QQ(3, 1) QQ(4, 1) }
     } else if (nch <= 128 * 4) {
-        switch ((nch + 127) / 128) {
-            QQ(3, 2) QQ(4, 2)
-        }
+        switch ((nch + 127) / 128) { QQ(3, 2) QQ(4, 2) }
     } else if (nch <= 256 * 8) {
-        switch ((nch + 255) / 256) {
-            QQ(3, 4) QQ(4, 4) QQ(5, 4) QQ(6, 4) QQ(7, 4) QQ(8, 4)
-#undef QQ
-        }
+        switch ((nch + 255) / 256) { QQ(3, 4) QQ(4, 4) QQ(5, 4) QQ(6, 4) QQ(7, 4) QQ(8, 4) }
     } else {
         hipLaunchKernelGGL(quant_rows_long_kernel, dim3(m), dim3(256), 0, st, x, ldx, xq, ldq, scale, m, k);
         return hipGetLastError();
     }
+#undef QQ
+#undef QL
     return hipErrorInvalidValue;
 }
 

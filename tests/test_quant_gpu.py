@@ -36,11 +36,13 @@ def _compare(xq_gpu, sx_gpu, xq_want, sx_want, what):
                            f"{[int(q[tuple(b)]) for b in bad[:5]]} vs {[int(xq_want[tuple(b)]) for b in bad[:5]]}")
 
 
-# (m, k): every kernel shape -- 1..4 chunks per lane with one wave per row, two and
-# four waves per row, up to 8 chunks per lane, and the two-pass kernel for rows
-# longer than 16384 -- with ragged row counts and chunk tails.
+# (m, k): every kernel shape -- under 512 rows four waves per row with 1..8 chunks per
+# lane; from 512 rows 1..4 chunks per lane with one wave per row, two and four waves per
+# row, up to 8 chunks per lane; the two-pass kernel for rows longer than 16384 -- with
+# ragged row counts and chunk tails.
 QUANT_SHAPES = [(1, 8), (5, 24), (7, 1000), (64, 256), (33, 2048), (9, 2056), (17, 4096), (4, 4104),
-                (12, 16384), (3, 16392), (2, 40000), (4099, 136), (18, 9472)]
+                (12, 16384), (3, 16392), (2, 40000), (4099, 136), (18, 9472),
+                (512, 8), (600, 1000), (520, 2056), (513, 4104), (530, 9472), (512, 16384)]
 
 
 @pytest.mark.parametrize("m,k", QUANT_SHAPES)
