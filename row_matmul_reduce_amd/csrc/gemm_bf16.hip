@@ -27,13 +27,11 @@ namespace rpl {
 struct Bf16Op {
     using Frag = bf16x8;
     using Acc = f32x4;
+    static constexpr bool STAGED = false;  // no per-row / per-column epilogue operands
     uint16_t *out;
     int n;
     __device__ static __forceinline__ Acc zero() { return Acc{0.f, 0.f, 0.f, 0.f}; }
-    __device__ static __forceinline__ Acc mfma(Frag a, Frag b, Acc c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-    // the same MFMA with the accumulators held in accumulation registers (four-wave engine)
+    // MFMA with the accumulators held in accumulation registers
     __device__ static __forceinline__ void mfma_acc(Acc &c, Frag a, Frag b) {
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
@@ -48,7 +46,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribu
 gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + BN) * KT_BYTES + PF_BYTES];
     Bf16Op op{out, g.n};
-    gemm_nt_wide<BN, PF>(g, op, smem);
+    gemm_nt_wide<BN, PF>(g, op, smem);  // not staged: no staging area
 }
 
 // ---------------------------------------------------------------- decode path

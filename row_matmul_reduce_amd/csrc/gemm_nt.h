@@ -7,7 +7,8 @@
 // copy that the xLLM pull request #1890 "feat: add FlashComm1 and MMRS fusion
 // support for Qwen3.5 NPU" caches in its review thread; here it is not needed).
 //
-// One workgroup computes a BM x BN output tile with WM x WN wavefronts.
+// One workgroup computes a 256 x 224 output tile with 2 x 2 wavefronts, 128 x 112
+// outputs per wave, the accumulators held in the accumulation registers.
 //
 // Staging.  A K step stages 128 bytes of every operand row (64 bf16 or 128
 // int8 values) in LDS, double-buffered.  Rows reach LDS straight from memory
@@ -28,14 +29,6 @@
 // them, so each line is touched about once per XCD rather than once per
 // sharer (half the L2 requests of a per-workgroup prefetch).  The barrier
 // waits for every load but that newest one.
-//
-// Schedule.  Per K step each wave reads its fragments for the two 32-deep
-// halves of the step from LDS and issues its MFMAs.  The second half's
-// fragments are read before the barrier that publishes the next buffer, and
-// the second half's MFMAs run after it, while the first-half fragments of the
-// next step are being read: the barrier and the LDS read latency hide behind
-// MFMA work.  The barrier waits only for this wave's DMA of the next buffer
-// and for its own reads of the current one.
 //
 // MFMA operand roles are swapped (A <- weight rows, B <- activation rows) so
 // that each lane's 4 accumulators are 4 consecutive output columns of one
@@ -103,222 +96,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
                                              RSRC_DWORD3);
 }
 
-// Op supplies: Frag (16-byte operand), Acc (4-lane accumulator), mfma(), zero(),
-// and the epilogue store(acc, m_row, n_col) of 4 consecutive columns.
-// Persistent tile loop: the grid has min(tiles, NUM_CU) workgroups and workgroup b
-// runs tiles b, b + grid, b + 2*grid, ... (grid is a multiple of 8 whenever it loops,
-// so a workgroup stays on one XCD's tile range).  A tile's first DMA is issued before
-// the previous tile's results are stored, so the stores overlap that load.
-// smem: 2 * (BM + BN) * KT_BYTES + PF_BYTES bytes of LDS.
-template <int BM, int BN, int WM, int WN, bool PRIO, int PF, int SCHED, class Op>
-__device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op &op, uint8_t *smem) {
-    constexpr int NW = WM * WN;
-    constexpr int TM = BM / WM, TN = BN / WN;
-    constexpr int FM = TM / 16, FN = TN / 16;
-    constexpr int GA = BM / 8, GB = BN / 8;  // 8-row (1 KB) groups per operand per step
-    static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "tile shape");
-    static_assert(NW >= 2 && BM / PF_SHARE_X <= 64, "prefetch slices: activation rows on wave 0, weight rows on wave 1");
-    using Frag = typename Op::Frag;
-    using Acc = typename Op::Acc;
+constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS DMA bases go in M0
-    const int wm0 = (wave / WN) * TM, wn0 = (wave % WN) * TN;
-    const int nt_m = (g.m_pad + BM - 1) / BM, nt_n = (g.n + BN - 1) / BN;
-    const int total = nt_m * nt_n;
-    const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
-    uint8_t *s0 = smem, *s1 = smem + (BM + BN) * KT_BYTES, *sink = smem + 2 * (BM + BN) * KT_BYTES;
-
-    // DMA lane mapping: lane writes LDS chunk (lane & 7) of row (lane >> 3) of its
-    // 8-row group, so it fetches logical chunk (lane & 7) ^ row.
-    const int lr = lane >> 3;
-    const int pc = (lane & 7) ^ lr;
-    const int frow = lane & 15, fchunk = lane >> 4;
-
-    __amdgpu_buffer_rsrc_t rx, rw;
-    auto issue = [&](int kt, uint8_t *buf) {
-        const int kb = kt * KT_BYTES + pc * 16;
-        const bool kin = kb < g.kbytes;
-#pragma unroll
-        for (int j = 0; j < (GA + NW - 1) / NW; ++j) {
-            const int gi = wave + j * NW;
-            if (GA % NW == 0 || gi < GA) {
-                const uint32_t v = kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < (GB + NW - 1) / NW; ++j) {
-            const int gj = wave + j * NW;
-            if (GB % NW == 0 || gj < GB) {
-                const uint32_t v = kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
-                                                         0, 0, 0);
-            }
-        }
-    };
-    // L2 prefetch of step kt.  The tiles an XCD runs at once form a band of group_m
-    // tile rows by about 8 tile columns (see tile_of_block), so 8 workgroups share each
-    // activation row and group_m share each weight row.  Each workgroup touches only its
-    // slice: activation rows [(tn % 8) * BM/8, +BM/8) on wave 0 and weight rows
-    // [(tm % group_m) * BN/group_m, +BN/group_m) on wave 1, one lane per row; the other
-    // waves issue an out-of-range load so that every wave has one prefetch in flight
-    // (the barrier's vmcnt counts on it).  A slice another workgroup misses only costs
-    // that line its lead; the DMA reads it regardless.
-    int tm = 0, tn = 0;
-    auto prefetch = [&](int kt) {
-        const int kb = kt * KT_BYTES;
-        uint32_t v = OOB_OFFSET;
-        if (wave == 0) {
-            constexpr int RX = BM / PF_SHARE_X;
-            if (lane < RX && kb < g.kbytes) v = (uint32_t)(((tn % PF_SHARE_X) * RX + lane) * g.ldx + kb);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
-        } else {
-            const int rw_rows = BN / g.group_m;
-            if (wave == 1 && lane < rw_rows && kb < g.kbytes)
-                v = (uint32_t)(((tm % g.group_m) * rw_rows + lane) * g.ldw + kb);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)sink, 4, v, 0, 0, 0);
-        }
-    };
-
-    Acc acc[FM][FN];
-    auto load_frags = [&](const uint8_t *sa, int half, Frag *xf, Frag *wf) {
-        const uint8_t *sb = sa + BM * KT_BYTES;
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-            xf[a] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
-                                                 sa + swz_off(wm0 + a * 16 + frow, half * 4 + fchunk)));
-#pragma unroll
-        for (int b = 0; b < FN; ++b)
-            wf[b] = __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(
-                                                 sb + swz_off(wn0 + b * 16 + frow, half * 4 + fchunk)));
-    };
-    auto mfmas = [&](const Frag *xf, const Frag *wf) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) acc[a][b] = Op::mfma(wf[b], xf[a], acc[a][b]);
-    };
-    // Empty asm statements that take the fragments make the compiler wait for their LDS
-    // reads at that point (cheap where used: the reads have long returned) and keep its
-    // wait bookkeeping exact, so no later MFMA waits on reads it does not need.
-    auto landed = [&](const Frag *xf, const Frag *wf) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a) asm volatile("" ::"v"(xf[a]));
-#pragma unroll
-        for (int b = 0; b < FN; ++b) asm volatile("" ::"v"(wf[b]));
-    };
-    // Workgroup barrier once this wave's reads of the current buffer have returned and
-    // its DMA into the next buffer has landed (vmcnt(PF ? 1 : 0): every load but the
-    // prefetch issued after that DMA).  sched_barrier keeps the compiler from moving
-    // work across it.
-    auto barrier = [&](const Frag *xf, const Frag *wf) {
-        __builtin_amdgcn_sched_barrier(0);
-        landed(xf, wf);
-        if (PF > 0) asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
-    auto store_tile = [&](int m0, int n0) {
-#pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            const int mrow = m0 + wm0 + a * 16 + frow;
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
-                if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
-            }
-        }
-    };
-
-    // DMA instructions this wave issues per step (the fewest any wave issues: vmcnt
-    // immediates below must not exceed any wave's own count).
-    constexpr int DMA_MIN = GA / NW + GB / NW;
-    constexpr int DMA_MAX = (GA + NW - 1) / NW + (GB + NW - 1) / NW;
-
-    Frag xa[FM], wa[FN], xb[FM], wb[FN];
-    int pm0 = 0, pn0 = 0;
-    bool have_prev = false;
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        tile_of_block(t, nt_m, nt_n, g.group_m, tm, tn);
-        const int m0 = tm * BM, n0 = tn * BN;
-        rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
-        rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
-        for (int d = 2; d < PF; ++d) prefetch(d);
-        issue(0, s0);  // every wave passed the previous tile's last barrier: no LDS reads it needs remain
-        if (have_prev) store_tile(pm0, pn0);
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) acc[a][b] = Op::zero();
-        if (ksteps > 1) {
-            issue(1, s1);  // stays in flight; everything older (step 0, the stores) must land
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(DMA_MIN) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        }
-        if (PRIO) __builtin_amdgcn_s_setprio(1);
-        load_frags(s0, 0, xa, wa);
-        landed(xa, wa);
-        uint8_t *cur = s0, *nxt = s1;
-        for (int kt = 0; kt < ksteps; ++kt) {
-            if (PF > 0) prefetch(kt + PF);  // past the end: out of range, reads nothing
-            load_frags(cur, 1, xb, wb);
-            mfmas(xa, wa);
-            barrier(xb, wb);  // step kt+1 has landed in nxt; nobody reads cur any more
-            // Second half: its MFMAs, the first-half fragment reads of step kt+1 and the DMA
-            // of step kt+2 into the buffer just released, interleaved one-for-one so the
-            // MFMA pipe never waits on instruction issue.  Both run unconditionally (one
-            // basic block to schedule): after the last step the reads fetch a buffer that
-            // is never used, and past the end the DMA offsets are out of range, which
-            // writes zeros into a buffer nobody reads before the next tile's own DMA
-            // (loads complete in issue order).
-            mfmas(xb, wb);
-            load_frags(nxt, 0, xa, wa);
-            if (SCHED == 2) issue(kt + 2, cur);
-#pragma unroll
-            for (int i = 0; i < FM + FN; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            }
-            if (SCHED == 2) {
-#pragma unroll
-                for (int i = 0; i < DMA_MAX; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA load
-                }
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, FM * FN, 0);  // the remaining MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            if (SCHED != 2 && kt + 2 < ksteps) issue(kt + 2, cur);
-            landed(xa, wa);
-            uint8_t *tmp = cur;
-            cur = nxt;
-            nxt = tmp;
-        }
-        if (PRIO) __builtin_amdgcn_s_setprio(0);
-        pm0 = m0;
-        pn0 = n0;
-        have_prev = true;
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
-    if (have_prev) store_tile(pm0, pn0);
-}
-
-// Four-wave form of the engine: a 256 x BN tile (BN = 224 or 256) on 2 x 2 waves,
-// 128 x BN/2 outputs per wave.  Per MFMA it reads a third fewer fragments from
-// LDS than the 8-wave form (16 fragment reads feed 64 MFMAs instead of 8 feeding
-// 16), and with one wave per SIMD each wave owns the whole register file: the
+// The engine: a 256 x BN tile (BN = 224 or 256) on 2 x 2 waves, 128 x BN/2
+// outputs per wave.  Per MFMA it reads a third fewer fragments from LDS than an
+// 8-wave layout (16 fragment reads feed 64 MFMAs instead of 8 feeding 16), and
+// with one wave per SIMD each wave owns the whole register file: the
 // 128 x 112 (or 128 x 128) fp32 accumulators live in the 256 accumulation
 // registers, pinned there by Op::mfma_acc (an MFMA written as inline assembly on
 // an "a"-constrained operand), which leaves the 256 vector registers to the two
 // fragment sets and the addressing.
 //
-// The step is the same as above (128 bytes of K per row, double-buffered, DMA
-// of step k+2 into the buffer released by step k's barrier, L2 prefetch of step
-// k+PF), but the interleave is explicit rather than requested from the
-// scheduler: each half-step is cut into FM+FN groups of MFMAs, each followed by
+// Per step: 128 bytes of K per row, double-buffered, DMA of step k+2 into the
+// buffer released by step k's barrier, L2 prefetch of step k+PF.  The interleave
+// is explicit rather than requested from the scheduler: each half-step is cut
+// into FM+FN groups of MFMAs, each followed by
 // one fragment read of the other half (and, in the second half, one DMA
 // instruction), with a sched_barrier after every group, so the issue order is
 // exactly that.  Each wave issues 8 + FN DMA instructions per step (activation
@@ -331,7 +123,8 @@ __device__ __forceinline__ void gemm_nt_persistent(const GemmShape &g, const Op 
 // the results of the last MFMAs of a tile are read only after enough wait
 // states (an s_nop tied to the accumulators of the last group; every earlier
 // group sits behind a sched_barrier and has long completed).
-// smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS.
+// smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
+// staged Op.
 template <int BN, int PF, class Op>
 __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, uint8_t *smem) {
     constexpr int BM = 256, NW = 4, WN = 2;
@@ -343,6 +136,7 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     static_assert(GA % NW == 0 && GB % NW == 0 && NA + NB == NR, "one DMA per fragment read");
     static_assert(BM / PF_SHARE_X <= 64, "activation prefetch slice fits one wave");
     constexpr int BUF = (BM + BN) * KT_BYTES;
+    constexpr int STAGE_FLOATS = BM + 256;  // one staging area: a value per tile row and per column
     using Frag = typename Op::Frag;
     using Acc = typename Op::Acc;
 
@@ -376,8 +170,8 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
                                                      0, 0, 0);
         }
     };
-    // Shared L2 prefetch as in the 8-wave form: activation slice on wave 0, weight slice
-    // on wave 1, an out-of-range load on the others (the barrier's vmcnt counts on one).
+    // Shared L2 prefetch: activation slice on wave 0, weight slice on wave 1, an
+    // out-of-range load on the others (the barrier's vmcnt counts on one).
     auto prefetch = [&](int kt) {
         const int kb = kt * KT_BYTES;
         uint32_t v = OOB_OFFSET;
@@ -443,23 +237,35 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         landed(xa, wa);
     };
     // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
-    auto store_tile = [&](int m0, int n0) {
+    // Ops with per-row and per-column epilogue operands (Op::STAGED) have them DMA'd into
+    // LDS at the start of each tile (Op::stage), so the epilogue reads LDS instead of
+    // waiting on global loads behind the next tile's DMA.  Two areas alternate by tile:
+    // a tile's staging never lands where the previous tile's epilogue still reads.
+    float *const stage_area = reinterpret_cast<float *>(smem + 2 * BUF + PF_BYTES);
+    auto store_tile = [&](int m0, int n0, int par) {
         constexpr int LAST = (NR - 1) * NM / NR;  // first MFMA of the last group
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
 #pragma unroll
         for (int i = LAST + 1; i < NM; ++i) asm volatile("" : "+a"(acc[i / FN][i % FN]));
+        const float *srow = stage_area + par * STAGE_FLOATS, *scol = srow + BM;
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
             const int mrow = m0 + wm0 + a * 16 + frow;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
                 const int ncol = n0 + wn0 + b * 16 + fchunk * 4;
-                if (mrow < g.m_pad && ncol < g.n) op.store(acc[a][b], mrow, ncol);
+                if (mrow < g.m_pad && ncol < g.n) {
+                    if constexpr (Op::STAGED)
+                        op.store_staged(acc[a][b], mrow, ncol, srow[mrow - m0],
+                                        *reinterpret_cast<const f32x4 *>(scol + (ncol - n0)));
+                    else
+                        op.store(acc[a][b], mrow, ncol);
+                }
             }
         }
     };
 
-    int pm0 = 0, pn0 = 0;
+    int pm0 = 0, pn0 = 0, par = 0;
     bool have_prev = false;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         int tm, tn;
@@ -469,10 +275,17 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
         pfx0 = (tn % PF_SHARE_X) * (BM / PF_SHARE_X);
         pfw0 = (tm % g.group_m) * pfw_rows;
+        if constexpr (Op::STAGED) {
+            float *srow = stage_area + (have_prev ? 1 - par : par) * STAGE_FLOATS;
+            op.stage(srow, srow + BM, m0, n0, wave, lane);  // lands before this prologue's barrier
+        }
         for (int d = 2; d < PF; ++d) prefetch(d);
 #pragma unroll
         for (int j = 0; j < NR; ++j) dma(0, s0, j);  // the previous tile's reads all ended at its barriers
-        if (have_prev) store_tile(pm0, pn0);
+        if (have_prev) {
+            store_tile(pm0, pn0, par);
+            par = 1 - par;
+        }
 #pragma unroll
         for (int j = 0; j < NR; ++j) dma(1, s1, j);  // out of range (zeros) when ksteps == 1
 #pragma unroll
@@ -499,24 +312,10 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         have_prev = true;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
-    if (have_prev) store_tile(pm0, pn0);
+    if (have_prev) store_tile(pm0, pn0, par);
 }
 
 // Grid of the persistent tile loop.
 __host__ __device__ inline int persistent_grid(int tiles) { return tiles < NUM_CU ? tiles : NUM_CU; }
-
-// Output tile width for the 256-row tile engine: 224 when it divides n and
-// packs the grid into fewer/fuller waves of workgroups over the 256 CUs than
-// 256 does, else 256.
-inline int pick_tile_n(int m_pad, int n) {
-    auto fill = [&](int bn) {
-        const long tiles = (long)((m_pad + 255) / 256) * ((n + bn - 1) / bn);
-        const long waves = (tiles + NUM_CU - 1) / NUM_CU;
-        const double useful = (double)m_pad * n;
-        return useful / ((double)waves * NUM_CU * 256.0 * bn);  // useful share of the issued tile waves
-    };
-    if (n % 224 == 0 && fill(224) > fill(256) + 1e-9) return 224;
-    return 256;
-}
 
 }  // namespace rpl
