@@ -60,9 +60,11 @@ def test_sum_partials_integers_exact_and_strided():
 
 
 # (m, n, tp, slice bounds): the decode o_proj share split over its 2 ranks, the 910C
-# operator's case (40 rows, hidden 2048, TP=2), uneven slices, 8 slices of the long-prefill row
+# operator's case (40 rows, hidden 2048, TP=2), uneven slices, 8 slices of the long-prefill row,
+# and slices wide enough for 2 to 6 chunks per lane
 SPLIT_CASES = [(4, 3584, 2, [0, 1792, 3584]), (40, 2048, 2, [0, 1024, 2048]),
-               (33, 520, 4, [0, 128, 264, 392, 520]), (2048, 5120, 8, list(range(0, 5121, 640)))]
+               (33, 520, 4, [0, 128, 264, 392, 520]), (2048, 5120, 8, list(range(0, 5121, 640))),
+               (17, 16384, 2, [0, 4096, 16384]), (9, 6008, 3, [0, 2056, 4104, 6008])]
 
 
 @pytest.mark.parametrize("m,n,tp,bounds", SPLIT_CASES, ids=lambda v: str(v) if not isinstance(v, list) else "slices")
