@@ -110,10 +110,9 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 // Per step: 128 bytes of K per row, double-buffered, DMA of step k+2 into the
 // buffer released by step k's barrier, L2 prefetch of step k+PF.  The interleave
 // is explicit rather than requested from the scheduler: each half-step is cut
-// into FM+FN groups of MFMAs, each followed by
-// one fragment read of the other half (and, in the second half, one DMA
-// instruction), with a sched_barrier after every group, so the issue order is
-// exactly that.  Each wave issues 8 + FN DMA instructions per step (activation
+// into FM+FN groups of MFMAs, each followed by one fragment read of the other
+// half (and, in the second half, one DMA instruction), with a sched_barrier
+// after every group, so the issue order is exactly that.  Each wave issues 8 + FN DMA instructions per step (activation
 // groups wave, wave+4, ...; weight groups likewise), as many as it reads
 // fragments.  The K loop is unrolled by two so that the buffer addresses are
 // constants.
@@ -123,6 +122,12 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 // the results of the last MFMAs of a tile are read only after enough wait
 // states (an s_nop tied to the accumulators of the last group; every earlier
 // group sits behind a sched_barrier and has long completed).
+//
+// Op supplies: Frag (16-byte operand) and Acc (4-lane accumulator) types, zero(),
+// mfma_acc(acc, weight_frag, activation_frag), and either store(acc, row, col) of 4
+// consecutive columns (STAGED = false) or, with STAGED = true, stage(rows, cols, m0,
+// n0, wave, lane), which DMAs a value per tile row and per tile column into LDS, and
+// store_staged(acc, row, col, row_value, column_values).
 // smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
 // staged Op.
 template <int BN, int PF, class Op>
