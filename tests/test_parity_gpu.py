@@ -229,8 +229,10 @@ def test_partial_row_stride_at_the_limit():
 
 
 # ------------------------------------------------------------------------ w8a8
+# the last two run more tiles than workgroups, so the scale staging alternates between its two LDS
+# areas (two tiles of two K steps; three tiles of one K step)
 W8A8_SHAPES = [(64, 512, 256, 2), (5, 24, 32, 2), (17, 40, 64, 8), (300, 520, 672, 2), (257, 264, 272, 4),
-               (512, 448, 256, 2), (512, 512, 512, 4), (4100, 4104, 160, 2)]
+               (512, 448, 256, 2), (512, 512, 512, 4), (4100, 4104, 160, 2), (8192, 5376, 48, 2)]
 
 
 def _w8a8_inputs(m, n, k, seed):
