@@ -24,8 +24,9 @@ epilogue and the token-row shard/gather around the exchange.  Every step cycles 
 twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
-from HIP events on the launch stream, the roofline of the dominant kernel, and
-the CPU oracle timed on a bounded sample of the same work.
+from HIP events on the launch stream, the roofline of the dominant kernel, the
+SCLK / MCLK levels sampled from sysfs while the same steps run, and the CPU
+oracle timed on a bounded sample of the same work.
 """
 from __future__ import annotations
 
@@ -372,6 +373,72 @@ def reduce_variants(torch, rpl, copies: int):
     return out
 
 
+def _dpm_files(torch):
+    """sysfs DPM tables (pp_dpm_sclk, pp_dpm_mclk) of the card the process runs on, or None."""
+    import glob
+    props = torch.cuda.get_device_properties(0)
+    want = None
+    if hasattr(props, "pci_bus_id") and hasattr(props, "pci_device_id"):
+        want = f"{getattr(props, 'pci_domain_id', 0):04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}"
+    cards = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        f = os.path.join(dev, "pp_dpm_sclk")
+        if os.path.exists(f) and os.access(f, os.R_OK):
+            cards.append((os.path.basename(os.path.realpath(dev)), dev))
+    if want is not None:
+        cards = [c for c in cards if c[0].lower().startswith(want)]
+    if len(cards) != 1:
+        return None
+    dev = cards[0][1]
+    return {k: os.path.join(dev, f"pp_dpm_{k}") for k in ("sclk", "mclk")}
+
+
+def _dpm_current_mhz(path):
+    """MHz of the level marked current ('*') in a pp_dpm_* table."""
+    try:
+        with open(path) as f:
+            for ln in f:
+                if ln.rstrip().endswith("*"):
+                    tok = ln.split(":", 1)[1].strip().split()[0].lower()
+                    return float(tok.replace("mhz", ""))
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def clocks_under_load(torch, step, launches: int):
+    """SCLK and MCLK while `launches` steps run back to back: the current DPM level of the card,
+    read from sysfs every millisecond on a host thread (outside the timed region; same work)."""
+    import threading
+    files = _dpm_files(torch)
+    if files is None:
+        return None
+    samples = {"sclk": [], "mclk": []}
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            for k, f in files.items():
+                v = _dpm_current_mhz(f)
+                if v is not None:
+                    samples[k].append(v)
+            time.sleep(0.001)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    for i in range(launches):
+        step(i)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    out = {"source": "current level of pp_dpm_sclk / pp_dpm_mclk, sampled every 1 ms while "
+                     f"{launches} steps ran", "card": os.path.dirname(files["sclk"])}
+    for k, v in samples.items():
+        out[f"{k}_mhz"] = ({"median": float(np.median(v)), "min": min(v), "max": max(v), "samples": len(v)}
+                          if v else None)
+    return out
+
+
 def token_rows(torch, rpl, copies: int):
     """The FlashComm1 token-row movement on the TP=8 long-prefill rows, HBM-resident: rank 0's block
     of the padded residual rows (16384 x 5120 -> 2048 x 5120) and the gather of the 8 ranks' blocks
@@ -498,6 +565,7 @@ def main():
     runner = path.run_graphs if small else path.run
     ms_per_step, kern, period = runner(args.steps, args.warmup)
     kernels = path.kernels_report(kern, period)
+    clocks = None if small else clocks_under_load(torch, path.step, 200)
     pn = path.pname
     if small:  # decode: bound by the weight stream
         value, unit = (wl.partial_bytes() + wl.reduce_bytes()) / (ms_per_step * 1e-3) / 1e9, "GB/s"
@@ -551,7 +619,7 @@ def main():
         "config": {"workload": wl.name, "m_tokens": wl.m, "k_full": wl.k_full, "tp": wl.tp, "k_shard": wl.k_shard,
                    "n": wl.n, "m_chunk": wl.m_chunk, "parallelism": f"one TP rank of {wl.tp} (peers emulated)",
                    "input_sets_rotated": sets_used},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "side": side,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "clocks": clocks, "side": side,
         "library_reference": reference,
         "kernel_sources_sha256_16": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
