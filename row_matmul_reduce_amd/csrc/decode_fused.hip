@@ -24,8 +24,9 @@
 // each row's partial sum of squares over its 16 columns to the workspace.  The
 // row norm needs every column: the workgroup that finishes last (a device-scope
 // counter in the workspace, incremented once per workgroup after a release
-// fence) sums the partial sums, then writes y for all columns from the fp32 h,
-// and resets the counter.  No workgroup waits for another, so nothing spins.
+// fence; the last one then takes an acquire fence) sums the partial sums, then
+// writes y for all columns from the fp32 h, and resets the counter.  No
+// workgroup waits for another, so nothing spins.
 #include "rpl_device.h"
 #include "rpl_launch.h"
 
@@ -131,18 +132,20 @@ decode_fused_kernel(FusedDecodeArgs a) {
             ss += __shfl_xor(ss, 32, 64);
             if (g == 0 && row < a.m) a.ss_ws[(int64_t)row * nblk + blockIdx.x] = ss;
         }
-        // Release this workgroup's h and partial sums at device scope (an L2 write-back on
-        // this multi-XCD part, so only the one wave that wrote them pays it), then count in.
-        __threadfence();
+        // Release this workgroup's h and partial sums at device (agent) scope -- an L2
+        // write-back on this multi-XCD part, so only the one wave that wrote them pays it --
+        // then count in.  A release fence, not a full one: nothing is read after it.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         if (lane == 0) last_flag = (atomicAdd(a.counter, 1u) == (unsigned)nblk - 1) ? 1 : 0;
     }
     __syncthreads();
     if (!last_flag) return;
 
-    // Last workgroup: every other workgroup's results are visible after an acquire fence.
-    // The first batch of h and gamma loads is issued before the partial sums are reduced,
-    // so the two round trips overlap.
-    __threadfence();
+    // Last workgroup: every other workgroup's results are visible after an acquire fence
+    // (the counter's read-modify-write read the increments that followed their release
+    // fences).  The first batch of h and gamma loads is issued before the partial sums are
+    // reduced, so the two round trips overlap.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     constexpr int U = 4;
     const int nch = a.n / 8;  // 8 outputs per chunk
     const int total = a.m * nch;
