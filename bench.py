@@ -232,6 +232,31 @@ class Path:
         period = a.elapsed_time(b) * 1e3 / steps
         return wall * 1e3 / steps, kern, period
 
+    def resident_partial_us(self, launches: int = 20, rounds: int = 5):
+        """The partial back to back on one input set (operands stay in the 256 MB MALL, and in L2
+        where they fit: the cache-resident figure) and, alternating with it in blocks of `launches`,
+        back to back over the rotated HBM-resident sets, so both see the same clock. Returns the
+        medians over `rounds` blocks (us per launch): (cache_resident, hbm_resident)."""
+        torch = self.torch
+        for _ in range(3):
+            self.partial(self.sets[0])
+        torch.cuda.synchronize()
+
+        def block(pick):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(launches):
+                self.partial(self.sets[pick(i)])
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / launches
+
+        res, rot = [], []
+        for _ in range(rounds):
+            res.append(block(lambda i: 0))
+            rot.append(block(lambda i: i % len(self.sets)))
+        return float(np.median(res)), float(np.median(rot))
+
     def kernels_report(self, kern, period):
         wl = self.wl
         pn, rn = self.pname, "reduce_rmsnorm"
@@ -566,6 +591,13 @@ def main():
     ms_per_step, kern, period = runner(args.steps, args.warmup)
     kernels = path.kernels_report(kern, period)
     clocks = None if small else clocks_under_load(torch, path.step, 200)
+    if not small:
+        ru, rr = path.resident_partial_us()
+        rate = "TFLOP/s" if not path.w8 else "TOP/s"
+        kernels[path.pname]["cache_resident"] = {
+            "what": "back to back on one input set (operands resident in MALL), alternating in blocks with the "
+                    "rotated HBM-resident sets; medians of 5 blocks of 20; not the headline",
+            "us": ru, rate: wl.gemm_flops() / (ru * 1e-6) / 1e12, "hbm_resident_us": rr}
     pn = path.pname
     if small:  # decode: bound by the weight stream
         value, unit = (wl.partial_bytes() + wl.reduce_bytes()) / (ms_per_step * 1e-3) / 1e9, "GB/s"
