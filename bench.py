@@ -21,7 +21,8 @@ steps (w8a8 both from int8 inputs and from the bf16 activation), plus the
 single-launch decode path (every shard's product + sum + residual + RMSNorm in one
 kernel) for a token chunk and for all rows, the all-reduce sum, the hidden-split
 epilogue and the token-row shard/gather around the exchange.  Every step cycles through several copies of its inputs (more than
-twice the 256 MB MALL), so operands come from HBM as a layer's weights do.
+twice the 256 MB MALL), so operands come from HBM as a layer's weights do.  Before the W
+warmup steps, untimed steps run for half a second so that the card is at its working clock.
 
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
 from HIP events on the launch stream, the roofline of the dominant kernel, the
@@ -168,10 +169,22 @@ class Path:
             if evs is not None:
                 evs[j][1].record()
 
+    def settle(self, seconds: float = 0.5):
+        """Untimed steps for at least `seconds` before the warmup steps: from idle the card takes
+        tens of milliseconds to reach its working clock, far longer than a few steps of this size."""
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                self.step(i)
+                i += 1
+            self.torch.cuda.synchronize()
+
     def run_graphs(self, steps: int, warmup: int):
         """Small (decode) paths: the host launch cost exceeds the kernels, so time HIP graphs
         that hold `steps` back-to-back launches; each replay runs them without host gaps."""
         torch = self.torch
+        self.settle()
         for i in range(max(warmup, len(self.sets))):
             self.step(i)
         torch.cuda.synchronize()
@@ -203,11 +216,12 @@ class Path:
         return wall * 1e3 / steps, kern, kern[self.pname]
 
     def run(self, steps: int, warmup: int):
-        """Time `steps` steps after `warmup`: wall ms per step (the steps alone, nothing recorded
+        """Time `steps` steps after the clock settles and `warmup` steps: wall ms per step (the steps alone, nothing recorded
         between their kernels), then the same number of steps again with HIP events around each
         kernel for the per-kernel means (us), and the back-to-back launch period of the partial
         alone (us; includes launch gaps)."""
         torch = self.torch
+        self.settle()
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
@@ -549,8 +563,8 @@ def cpu_baseline(wl, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill", choices=list(WORKLOAD_IDS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
