@@ -18,7 +18,8 @@
 //    the whole weight), so each workgroup owns 16 output columns, its waves
 //    split K, every wave issues all of its weight loads before its first MFMA,
 //    and the per-wave partial sums are added in LDS (no atomics: the result
-//    is deterministic).
+//    is deterministic).  With 8 or fewer rows one activation load carries
+//    two (four) K steps, moved into place with row shifts between lanes.
 #include "gemm_nt.h"
 #include "rpl_launch.h"
 
@@ -53,9 +54,27 @@ gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_BATCH = 16;  // K steps (32 values each) whose loads are issued together
 
+// Lane i of the result takes lane i + SH of v within each row of 16 lanes (zero past the row).
+template <int SH>
+__device__ __forceinline__ u32x4 lanes_down(u32x4 v) {
+    static_assert(SH > 0 && SH < 16, "a row shift");
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_update_dpp(0u, v[q], 0x100 + SH, 0xF, 0xF, true);
+    return r;
+}
+
+// XP: K steps per activation load.  The MFMA takes token row r from lanes r, r+16, r+32,
+// r+48; with m_pad <= 16/XP rows the other lanes of a load would be idle, so lane row
+// r16 loads token row r16 % (16/XP) of step s + r16 / (16/XP), and step s + q reads its
+// fragment q*16/XP lanes down.  Output rows >= 16/XP then hold other steps' products;
+// they are pad rows past m_pad and never stored.
+template <int XP>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * DEC_WAVES, 64 * DEC_WAVES)))
 gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint16_t *__restrict__ w,
                         int64_t ldw, uint16_t *__restrict__ out, int m, int m_pad, int n, int k) {
+    constexpr int XR = 16 / XP;  // token rows one load carries per step
+    static_assert(DEC_BATCH % XP == 0, "whole activation loads per batch");
     __shared__ f32x4 red[DEC_WAVES - 1][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n0 = blockIdx.x * 16;
@@ -65,25 +84,39 @@ gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint1
 
     const int r16 = lane & 15, g = lane >> 4;
     const int wrow = n0 + r16;
-    const bool wrow_ok = wrow < n, xrow_ok = r16 < m;
+    const int xrow = r16 % XR, xsub = r16 / XR;
+    const bool wrow_ok = wrow < n, xrow_ok = xrow < m;
     const uint16_t *wp = w + (int64_t)(wrow_ok ? wrow : 0) * ldw + g * 8;
-    const uint16_t *xp = x + (int64_t)(xrow_ok ? r16 : 0) * ldx + g * 8;
+    const uint16_t *xp = x + (int64_t)(xrow_ok ? xrow : 0) * ldx + g * 8;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = s_begin; s0 < s_end; s0 += DEC_BATCH) {
-        u32x4 wf[DEC_BATCH], xf[DEC_BATCH];
+        u32x4 wf[DEC_BATCH], xf[DEC_BATCH / XP];
 #pragma unroll
         for (int j = 0; j < DEC_BATCH; ++j) {
             const int s = s0 + j;
-            const int kel = s * 32 + g * 8;
-            const bool live = s < s_end && kel < k;
+            const bool live = s < s_end && s * 32 + g * 8 < k;
             wf[j] = (live && wrow_ok) ? ld16(wp + s * 32) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < DEC_BATCH / XP; ++j) {
+            const int s = s0 + j * XP + xsub;
+            const bool live = s < s_end && s * 32 + g * 8 < k;
             xf[j] = (live && xrow_ok) ? ld16(xp + s * 32) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int j = 0; j < DEC_BATCH; ++j)
+        for (int j = 0; j < DEC_BATCH; ++j) {
+            u32x4 xv = xf[j / XP];
+            if constexpr (XP == 2) {
+                if (j % 2) xv = lanes_down<8>(xv);
+            } else if constexpr (XP == 4) {
+                if (j % 4 == 1) xv = lanes_down<4>(xv);
+                if (j % 4 == 2) xv = lanes_down<8>(xv);
+                if (j % 4 == 3) xv = lanes_down<12>(xv);
+            }
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[j]),
-                                                          __builtin_bit_cast(bf16x8, xf[j]), acc, 0, 0, 0);
+                                                          __builtin_bit_cast(bf16x8, xv), acc, 0, 0, 0);
+        }
     }
     if (wave > 0) red[wave - 1][lane] = acc;
     __syncthreads();
@@ -102,8 +135,13 @@ gemm_bf16_decode_kernel(const uint16_t *__restrict__ x, int64_t ldx, const uint1
 hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w, int64_t ldw, uint16_t *out,
                                int m, int m_pad, int n, int k, hipStream_t st) {
     if (m_pad <= 16) {
-        hipLaunchKernelGGL(gemm_bf16_decode_kernel, dim3((n + 15) / 16), dim3(64 * DEC_WAVES), 0, st, x, ldx, w,
-                           ldw, out, m, m_pad, n, k);
+        const dim3 grid((n + 15) / 16), block(64 * DEC_WAVES);
+        if (m_pad <= 4)
+            hipLaunchKernelGGL(gemm_bf16_decode_kernel<4>, grid, block, 0, st, x, ldx, w, ldw, out, m, m_pad, n, k);
+        else if (m_pad <= 8)
+            hipLaunchKernelGGL(gemm_bf16_decode_kernel<2>, grid, block, 0, st, x, ldx, w, ldw, out, m, m_pad, n, k);
+        else
+            hipLaunchKernelGGL(gemm_bf16_decode_kernel<1>, grid, block, 0, st, x, ldx, w, ldw, out, m, m_pad, n, k);
         return hipGetLastError();
     }
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),

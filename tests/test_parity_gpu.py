@@ -46,6 +46,9 @@ SMALL_SHAPES = [
     (5, 24, 32, 2),        # m not divisible by tp: one zero pad row (decode kernel)
     (3, 40, 64, 4),        # decode kernel, ragged column tile
     (16, 264, 2048, 2),    # decode kernel at m_pad = 16, K split over every wave
+    (4, 136, 4000, 2),     # decode kernel, m_pad = 4: four K steps per activation load, K tail
+    (7, 72, 2608, 2),      # decode kernel, m_pad = 8: two K steps per activation load, K tail
+    (2, 24, 1040, 1),      # decode kernel, m_pad = 2, 32.5 K steps
     (8, 3584, 3584, 2),    # decode o_proj shape
     (17, 64, 128, 8),      # tile kernel with bounds checks, m_pad = 24, a single K step
     (300, 520, 656, 2),    # ragged m, n and K (k_shard = 328)
@@ -76,7 +79,8 @@ def test_partial_small(m, n, k_full, tp):
         assert np.all(got[m:] == 0), "pad rows must be zero"
 
 
-@pytest.mark.parametrize("m,n,k", [(8, 64, 64), (13, 48, 96), (300, 264, 272), (512, 512, 256)])
+@pytest.mark.parametrize("m,n,k", [(8, 64, 64), (13, 48, 96), (3, 40, 1000), (7, 56, 2056), (300, 264, 272),
+                                   (512, 512, 256)])
 def test_partial_exact_cases(m, n, k):
     say(f"[exact] m={m} n={n} k={k}")
     rng = np.random.default_rng(m * n)
