@@ -509,26 +509,40 @@ def token_rows(torch, rpl, copies: int):
                            "shard_frac_hbm": bs / (us_s * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
 
-def library_reference(path, torch, steps: int):
+def library_reference(path, torch, rounds: int = 6, block: int = 20):
     """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
-    HBM-resident input sets, same stream and timing method, to show what the chip gives under the
-    bench's sustained load.  Its result is not used anywhere."""
+    HBM-resident input sets.  It and the library's partial are timed the same way, per launch with
+    HIP events, in alternating blocks of `block` launches so both see the same clock; medians over
+    all launches.  Its result is not used anywhere."""
     wl = path.wl
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(3):
-        d = path.sets[i % len(path.sets)]
+
+    def vendor(d):
         torch.matmul(d["x"], d["w"].t())
+
+    def timed(fn):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(block)]
+        for i, (a, b) in enumerate(evs):
+            d = path.sets[i % len(path.sets)]
+            a.record()
+            fn(d)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+    for fn in (vendor, path.partial):
+        for i in range(5):
+            fn(path.sets[i % len(path.sets)])
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        d = path.sets[i % len(path.sets)]
-        a.record()
-        torch.matmul(d["x"], d["w"].t())
-        b.record()
-    torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    ours, theirs = [], []
+    for _ in range(rounds):
+        ours += timed(path.partial)
+        theirs += timed(vendor)
+    us, own = float(np.median(theirs)), float(np.median(ours))
     rate = wl.gemm_flops() / (us * 1e-6) / 1e12
-    return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation",
-            "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS}
+    return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation; it and "
+                    "the library's partial timed per launch in alternating blocks, medians",
+            "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS,
+            "partial_us_same_method": own, "partial_over_vendor_time": own / us}
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -646,7 +660,7 @@ def main():
     sets_used = len(path.sets)
     reference = None
     if not path.w8 and not small and not args.no_side:
-        reference = library_reference(path, torch, args.steps)
+        reference = library_reference(path, torch)
     del path
     torch.cuda.empty_cache()
 
@@ -661,6 +675,8 @@ def main():
                 s_ms, s_kern, s_period = sp.run(10, 3)
             side[key] = {"workload": swl.name, "ms_per_step": s_ms, "input_sets_rotated": len(sp.sets),
                          "kernels": sp.kernels_report(s_kern, s_period)}
+            if key == "long_prefill":
+                side[key]["library_reference"] = library_reference(sp, torch)
             del sp
             torch.cuda.empty_cache()
 

@@ -25,10 +25,12 @@
 // less than the latency of HBM under load.  So each step also touches the
 // lines of step k+PF (PF = 3) -- one 4-byte DMA per 128-byte line into a
 // 256-byte LDS sink that is never read -- so that the real DMA finds them in
-// L2.  The workgroups of an XCD that share a row split its prefetch between
-// them, so each line is touched about once per XCD rather than once per
-// sharer (half the L2 requests of a per-workgroup prefetch).  The barrier
-// waits for every load but that newest one.
+// L2.  The workgroups of an XCD that share activation rows split their
+// prefetch between them, so each line is touched about once per XCD rather
+// than once per sharer (half the L2 requests of a per-workgroup prefetch).
+// Only the activation is prefetched: the four workgroups of an XCD that share
+// a weight tile request its lines together anyway, and prefetching it as well
+// measured 2% slower.  The barrier waits for every load but the newest one.
 //
 // MFMA operand roles are swapped (A <- weight rows, B <- activation rows) so
 // that each lane's 4 accumulators are 4 consecutive output columns of one
@@ -155,10 +157,9 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     const int lr = lane >> 3;
     const int pc = (lane & 7) ^ lr;
     const int frow = lane & 15, fchunk = lane >> 4;
-    const int pfw_rows = BN / g.group_m;
 
     __amdgpu_buffer_rsrc_t rx, rw;
-    int pfx0 = 0, pfw0 = 0;  // first row of this workgroup's prefetch slice (activation, weight)
+    int pfx0 = 0;  // first row of this workgroup's activation prefetch slice
     // DMA instruction j of step kt into buf: activation group j*NW + wave (j < NA), else
     // weight group (j-NA)*NW + wave.  j is a compile-time constant at every call.
     auto dma = [&](int kt, uint8_t *buf, int j) {
@@ -175,18 +176,13 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
                                                      0, 0, 0);
         }
     };
-    // Shared L2 prefetch: activation slice on wave 0, weight slice on wave 1, an
-    // out-of-range load on the others (the barrier's vmcnt counts on one).
+    // Shared L2 prefetch of the activation slice on wave 0, an out-of-range load on
+    // the others (the barrier's vmcnt counts on one).
     auto prefetch = [&](int kt) {
         const int kb = kt * KT_BYTES;
         uint32_t v = OOB_OFFSET;
-        if (wave == 0) {
-            if (lane < BM / PF_SHARE_X && kb < g.kbytes) v = (uint32_t)((pfx0 + lane) * g.ldx + kb);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
-        } else {
-            if (wave == 1 && lane < pfw_rows && kb < g.kbytes) v = (uint32_t)((pfw0 + lane) * g.ldw + kb);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)sink, 4, v, 0, 0, 0);
-        }
+        if (wave == 0 && lane < BM / PF_SHARE_X && kb < g.kbytes) v = (uint32_t)((pfx0 + lane) * g.ldx + kb);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)sink, 4, v, 0, 0, 0);
     };
 
     Acc acc[FM][FN];
@@ -279,7 +275,6 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
         rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
         pfx0 = (tn % PF_SHARE_X) * (BM / PF_SHARE_X);
-        pfw0 = (tm % g.group_m) * pfw_rows;
         if constexpr (Op::STAGED) {
             float *srow = stage_area + (have_prev ? 1 - par : par) * STAGE_FLOATS;
             op.stage(srow, srow + BM, m0, n0, wave, lane);  // lands before this prologue's barrier
