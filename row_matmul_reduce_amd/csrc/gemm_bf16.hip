@@ -42,12 +42,12 @@ struct Bf16Op {
     }
 };
 
-template <int BN, int PF>
+template <int BN, int PF, bool KTAIL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + BN) * KT_BYTES + PF_BYTES];
     Bf16Op op{out, g.n};
-    gemm_nt_wide<BN, PF>(g, op, smem);  // not staged: no staging area
+    gemm_nt_wide<BN, PF, KTAIL>(g, op, smem);  // not staged: no staging area
 }
 
 // ---------------------------------------------------------------- decode path
@@ -147,7 +147,10 @@ hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),
                 ldx * 2, ldw * 2, m, m_pad, n, k * 2, 4};
     const int nt = ((m_pad + 255) / 256) * ((n + 223) / 224);
-    hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
+    if (g.kbytes % KT_BYTES)
+        hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, true>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
+    else
+        hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, false>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
     return hipGetLastError();
 }
 

@@ -63,11 +63,11 @@ struct W8a8Op {
     }
 };
 
-template <int BN, int PF>
+template <int BN, int PF, bool KTAIL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_w8a8_wide_kernel(GemmShape g, W8a8Op op) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + BN) * KT_BYTES + PF_BYTES + WIDE_STAGE_BYTES];
-    gemm_nt_wide<BN, PF>(g, op, smem);
+    gemm_nt_wide<BN, PF, KTAIL>(g, op, smem);
 }
 
 hipError_t launch_partial_w8a8(const int8_t *xq, int64_t ldx, const float *sx, const int8_t *wq, int64_t ldw,
@@ -77,7 +77,10 @@ hipError_t launch_partial_w8a8(const int8_t *xq, int64_t ldx, const float *sx, c
                 k, 4};
     W8a8Op op{out, acc, sx, sw, m, n};
     const int nt = ((m_pad + 255) / 256) * ((n + 223) / 224);
-    hipLaunchKernelGGL((gemm_w8a8_wide_kernel<224, 3>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, op);
+    if (g.kbytes % KT_BYTES)
+        hipLaunchKernelGGL((gemm_w8a8_wide_kernel<224, 3, true>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, op);
+    else
+        hipLaunchKernelGGL((gemm_w8a8_wide_kernel<224, 3, false>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, op);
     return hipGetLastError();
 }
 
