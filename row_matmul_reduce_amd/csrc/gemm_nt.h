@@ -88,14 +88,25 @@ __device__ __forceinline__ int swz_off(int row, int chunk) { return row * KT_BYT
 
 // Buffer descriptor over rows [r0, rows) of a row-major operand with row stride ld bytes
 // and kbytes valid bytes per row; rows at or past `rows` read as zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int r0, int rows, int64_t ld,
-                                                            int kbytes) {
+// The same as a base and a record count, for descriptors rebuilt per K step.
+struct TileSpan {
+    const uint8_t *base;
+    uint32_t nrec;
+};
+__device__ __forceinline__ TileSpan tile_span(const uint8_t *base, int r0, int rows, int64_t ld, int kbytes) {
     const bool live = r0 < rows;
     const int64_t start = (int64_t)r0 * ld;
     const int64_t span = (int64_t)(rows - 1) * ld + kbytes;  // bytes from row 0 to the last valid byte
     const uint32_t nrec = __builtin_amdgcn_readfirstlane(live ? (uint32_t)min<int64_t>(span - start, 0x7FFFFFFF) : 0u);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base + (live ? start : 0)), (short)0, (int)nrec,
+    return TileSpan{base + (live ? start : 0), nrec};
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const TileSpan &t, bool live) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(t.base), (short)0, live ? (int)t.nrec : 0,
                                              RSRC_DWORD3);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base, int r0, int rows, int64_t ld,
+                                                            int kbytes) {
+    return span_rsrc(tile_span(base, r0, rows, ld, kbytes), true);
 }
 
 constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
@@ -133,8 +144,8 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 // smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
 // staged Op.  KTAIL: K is not a whole number of steps (kbytes % KT_BYTES != 0), so the
 // last step's chunks past K are cut lane by lane; without a tail only whole steps past
-// the end are cut, by one uniform test per step (no per-lane select in the DMA
-// addressing: 2-3% faster on the prefill shares).
+// the end are cut, by one uniform test per step, and the DMA addressing needs no
+// vector instruction at all (2-3% faster on the prefill shares than the per-lane form).
 template <int BN, int PF, bool KTAIL, class Op>
 __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, uint8_t *smem) {
     constexpr int BM = 256, NW = 4, WN = 2;
@@ -162,26 +173,44 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     const int frow = lane & 15, fchunk = lane >> 4;
 
     __amdgpu_buffer_rsrc_t rx, rw;
+    TileSpan sx{}, sw{};  // the same tiles as base and record count (per-step descriptors)
     int pfx0 = 0;  // first row of this workgroup's activation prefetch slice
     // DMA instruction j of step kt into buf: activation group j*NW + wave (j < NA), else
     // weight group (j-NA)*NW + wave.  j is a compile-time constant at every call.
-    // Row offsets stay below 2^31 (255 rows of a stride under 2^23 bytes), so adding
-    // OOB_OFFSET cannot wrap and lands past every record count.
+    // With a K tail each lane's offset is cut to OOB_OFFSET past K.  Without one the
+    // per-lane offset is the same at every step (the compiler keeps it in a register)
+    // and the step's byte offset goes in the scalar offset; a step past the end gets a
+    // descriptor with no records, so its loads read nothing.  Either way a lane's byte
+    // is row * ld + k, inside the row's K bytes or out of range.
     auto dma = [&](int kt, uint8_t *buf, int j) {
-        const int kb = kt * KT_BYTES + pc * 16;
-        const bool kin = kb < g.kbytes;  // KTAIL: per lane
-        const uint32_t kstep = kt * KT_BYTES < g.kbytes ? (uint32_t)(kt * KT_BYTES) : OOB_OFFSET;  // uniform
-        if (j < NA) {
-            const int gi = j * NW + wave;
-            const uint32_t v = KTAIL ? (kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET)
-                                     : (uint32_t)((gi * 8 + lr) * g.ldx + pc * 16) + kstep;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
+        if constexpr (KTAIL) {
+            const int kb = kt * KT_BYTES + pc * 16;
+            const bool kin = kb < g.kbytes;
+            if (j < NA) {
+                const int gi = j * NW + wave;
+                const uint32_t v = kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
+            } else {
+                const int gj = (j - NA) * NW + wave;
+                const uint32_t v = kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
+                                                         0, 0, 0);
+            }
         } else {
-            const int gj = (j - NA) * NW + wave;
-            const uint32_t v = KTAIL ? (kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET)
-                                     : (uint32_t)((gj * 8 + lr) * g.ldw + pc * 16) + kstep;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
-                                                     0, 0, 0);
+            const bool live = kt * KT_BYTES < g.kbytes;
+            const int kstep = live ? kt * KT_BYTES : 0;
+            if (j < NA) {
+                const int gi = j * NW + wave;
+                const uint32_t v = (uint32_t)((gi * 8 + lr) * g.ldx + pc * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sx, live), (lds_void_t *)(buf + gi * 1024), 16, v,
+                                                         kstep, 0, 0);
+            } else {
+                const int gj = (j - NA) * NW + wave;
+                const uint32_t v = (uint32_t)((gj * 8 + lr) * g.ldw + pc * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sw, live),
+                                                         (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v, kstep,
+                                                         0, 0);
+            }
         }
     };
     // Shared L2 prefetch of the activation slice on wave 0, an out-of-range load on
@@ -280,8 +309,10 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         int tm, tn;
         tile_of_block(t, nt_m, nt_n, g.group_m, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        rx = tile_rsrc(g.x, m0, g.m, g.ldx, g.kbytes);
-        rw = tile_rsrc(g.w, n0, g.n, g.ldw, g.kbytes);
+        sx = tile_span(g.x, m0, g.m, g.ldx, g.kbytes);
+        sw = tile_span(g.w, n0, g.n, g.ldw, g.kbytes);
+        rx = span_rsrc(sx, true);
+        rw = span_rsrc(sw, true);
         pfx0 = (tn % PF_SHARE_X) * (BM / PF_SHARE_X);
         if constexpr (Op::STAGED) {
             float *srow = stage_area + (have_prev ? 1 - par : par) * STAGE_FLOATS;
