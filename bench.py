@@ -59,7 +59,8 @@ KERNEL_SOURCES = {
     "token_rows": ["token_rows.hip", "rpl_device.h"],
 }
 # kernels that live in a shared source file
-KERNEL_KEY = {"sum_partials": "reduce_variants", "slice_sumsq": "reduce_variants", "slice_apply": "reduce_variants"}
+KERNEL_KEY = {"sum_partials": "reduce_variants", "slice_sumsq": "reduce_variants", "slice_apply": "reduce_variants",
+              "token_rows_gather": "token_rows", "token_rows_shard": "token_rows"}
 WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
 
@@ -198,13 +199,18 @@ class Path:
             torch.cuda.synchronize()
             return g
 
-        def per_launch_us(g):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / steps
+        def per_launch_us(g, nm, replays=5):
+            # the mean per launch of one replay; over `replays` replays, their mean and median
+            ts = []
+            for _ in range(replays):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3 / steps)
+            self.medians[nm] = float(np.median(ts))
+            return float(np.mean(ts))
 
         g_step = capture(lambda d, i: self.step(i))
         torch.cuda.synchronize()
@@ -212,13 +218,14 @@ class Path:
         g_step.replay()          # exactly `steps` steps
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kern = {nm: per_launch_us(capture(lambda d, i, fn=fn: fn(d))) for nm, fn in zip(self.names, self.stages)}
+        self.medians = {}
+        kern = {nm: per_launch_us(capture(lambda d, i, fn=fn: fn(d)), nm) for nm, fn in zip(self.names, self.stages)}
         return wall * 1e3 / steps, kern, kern[self.pname]
 
     def run(self, steps: int, warmup: int):
         """Time `steps` steps after the clock settles and `warmup` steps: wall ms per step (the steps alone, nothing recorded
         between their kernels), then the same number of steps again with HIP events around each
-        kernel for the per-kernel means (us), and the back-to-back launch period of the partial
+        kernel for the per-kernel means and medians (us), and the back-to-back launch period of the partial
         alone (us; includes launch gaps)."""
         torch = self.torch
         self.settle()
@@ -237,6 +244,8 @@ class Path:
         torch.cuda.synchronize()
         kern = {nm: float(np.mean([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
                 for j, nm in enumerate(self.names)}
+        self.medians = {nm: float(np.median([evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(steps)])) * 1e3
+                        for j, nm in enumerate(self.names)}
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for i in range(steps):
@@ -278,18 +287,20 @@ class Path:
         pu = kern[pn]
         peak = PEAK_I8_TOPS if self.w8 else PEAK_BF16_TFLOPS
         rate = flop / (pu * 1e-6) / 1e12
-        rep = {pn: {"us": pu, "back_to_back_period_us": period, "flop": flop,
+        med = getattr(self, "medians", {})
+        rep = {pn: {"us": pu, "us_median": med.get(pn), "back_to_back_period_us": period, "flop": flop,
                     ("TOP/s" if self.w8 else "TFLOP/s"): rate, "frac_mfma_peak": rate / peak,
                     "bytes": pbytes, "GB/s": pbytes / (pu * 1e-6) / 1e9}}
         if self.w8:
             rep[pn]["frac_bf16_peak_figure"] = rate / PEAK_BF16_TFLOPS
         rep[pn]["frac_hbm"] = rep[pn]["GB/s"] / PEAK_HBM_GBS
         ru = kern[rn]
-        rep[rn] = {"us": ru, "bytes": rbytes, "GB/s": rbytes / (ru * 1e-6) / 1e9}
+        rep[rn] = {"us": ru, "us_median": med.get(rn), "bytes": rbytes, "GB/s": rbytes / (ru * 1e-6) / 1e9}
         rep[rn]["frac_hbm"] = rep[rn]["GB/s"] / PEAK_HBM_GBS
         if self.dyn:
             qu, qb = kern["quant_per_token"], wl.quant_bytes()
-            rep["quant_per_token"] = {"us": qu, "bytes": qb, "GB/s": qb / (qu * 1e-6) / 1e9,
+            rep["quant_per_token"] = {"us": qu, "us_median": med.get("quant_per_token"), "bytes": qb,
+                                      "GB/s": qb / (qu * 1e-6) / 1e9,
                                       "frac_hbm": qb / (qu * 1e-6) / 1e9 / PEAK_HBM_GBS}
         return rep
 
