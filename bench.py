@@ -556,23 +556,46 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
             "partial_us_same_method": own, "partial_over_vendor_time": own / us}
 
 
-def cpu_baseline(wl, budget_s: float):
-    """The CPU oracle on the first R token rows of the same step (R sized to the time budget)."""
+def cpu_baseline(wl, budget_s: float, dynamic: bool = False):
+    """The CPU oracle on the first R token rows of the same step (R sized to the time budget).
+    For the w8a8 path the step is the int8 partial rows (preceded, for w8a8_dynamic, by the
+    per-token quantiser of those rows) and the chunk reduce/RMSNorm."""
     import oracle
     from row_matmul_reduce_amd import synth
     threads = oracle.num_threads()
     mc = wl.m_chunk
-    x0, w0 = synth.x_shard(wl, 0, rows=mc), synth.w_shard(wl, 0)
-    peers = [(synth.x_shard(wl, s, rows=mc), synth.w_shard(wl, s)) for s in range(1, wl.tp)]
     res, gam = synth.residual_chunk(wl), synth.gamma(wl)
+    if wl.kind == "w8a8":
+        if dynamic:
+            xb = synth.x_shard(wl, 0, rows=mc)
+            wq0, sw0 = synth.w8a8_weight(wl, 0)
+        else:
+            xq0, sx0, wq0, sw0 = synth.w8a8_inputs(wl, rows=mc, shard=0)
+        peers = [synth.w8a8_inputs(wl, rows=mc, shard=s) for s in range(1, wl.tp)]
 
-    def run(rows):
-        r = np.arange(rows, dtype=np.int64)
-        peer_parts = [oracle.partial_rows(px, pw, mc, rows=r) for px, pw in peers]  # arrived data: untimed
-        t = time.perf_counter()
-        own = oracle.partial_rows(x0, w0, wl.m, rows=r, tp=wl.tp)
-        oracle.reduce_chunk_rmsnorm([own] + peer_parts, res[:rows], gam, wl.eps)
-        return time.perf_counter() - t
+        def run(rows):
+            r = np.arange(rows, dtype=np.int64)
+            peer_parts = [oracle.w8a8_rows(pq, psx, pwq, psw, mc, rows=r)[0]
+                          for pq, psx, pwq, psw in peers]  # arrived data: untimed
+            t = time.perf_counter()
+            if dynamic:
+                xq, sx = oracle.quant_per_token(xb, rows)
+            else:
+                xq, sx = xq0[:rows], sx0[:rows]
+            own = oracle.w8a8_rows(xq, sx, wq0, sw0, rows, rows=r)[0]
+            oracle.reduce_chunk_rmsnorm([own] + peer_parts, res[:rows], gam, wl.eps)
+            return time.perf_counter() - t
+    else:
+        x0, w0 = synth.x_shard(wl, 0, rows=mc), synth.w_shard(wl, 0)
+        peers = [(synth.x_shard(wl, s, rows=mc), synth.w_shard(wl, s)) for s in range(1, wl.tp)]
+
+        def run(rows):
+            r = np.arange(rows, dtype=np.int64)
+            peer_parts = [oracle.partial_rows(px, pw, mc, rows=r) for px, pw in peers]  # arrived data: untimed
+            t = time.perf_counter()
+            own = oracle.partial_rows(x0, w0, wl.m, rows=r, tp=wl.tp)
+            oracle.reduce_chunk_rmsnorm([own] + peer_parts, res[:rows], gam, wl.eps)
+            return time.perf_counter() - t
 
     pilot = min(8, mc)
     t_pilot = run(pilot)
@@ -586,10 +609,13 @@ def cpu_baseline(wl, budget_s: float):
         nbytes = 2.0 * (wl.n * wl.k_shard + rows * wl.k_shard + rows * wl.n) + wl.tp * 2.0 * rows * wl.n
         value, unit = nbytes / dt / 1e9, "GB/s"
     else:
-        value, unit = 2.0 * rows * wl.n * wl.k_shard / dt / 1e12, "TFLOP/s"
+        value, unit = 2.0 * rows * wl.n * wl.k_shard / dt / 1e12, ("TOP/s" if wl.kind == "w8a8" else "TFLOP/s")
+    what = "partial rows + chunk reduce/RMSNorm of those rows"
+    if wl.kind == "w8a8":
+        what = ("per-token quantiser, " if dynamic else "") + "int8 partial rows + chunk reduce/RMSNorm of those rows"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "cpu_model": _cpu_model(),
-            "sample": f"the step restricted to the first {rows} of {wl.m} token rows (partial rows + "
-                      f"chunk reduce/RMSNorm of those rows), fp64 C oracle with {threads} OpenMP threads, "
+            "sample": f"the step restricted to the first {rows} of {wl.m} token rows ({what}), "
+                      f"fp64 C oracle with {threads} OpenMP threads, "
                       f"{dt * reps:.1f} s" + (f" over {reps} repeats" if reps > 1 else "")}
 
 
@@ -662,7 +688,7 @@ def main():
         roofline = {"bound": "hbm", "kernel": pn, "achieved": kernels[pn]["GB/s"], "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": kernels[pn]["frac_hbm"], "traffic": load_traffic(pn, wl.name)}
     else:
-        value, unit = wl.gemm_flops() / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        value, unit = wl.gemm_flops() / (ms_per_step * 1e-3) / 1e12, ("TOP/s" if path.w8 else "TFLOP/s")
         peak = PEAK_I8_TOPS if path.w8 else PEAK_BF16_TFLOPS
         rate = kernels[pn]["TOP/s" if path.w8 else "TFLOP/s"]
         roofline = {"bound": "mfma", "kernel": pn, "achieved": rate, "peak": peak,
@@ -701,8 +727,8 @@ def main():
         torch.cuda.empty_cache()
 
     cpu = None
-    if not args.no_cpu_baseline and wl.kind != "w8a8":
-        cpu = cpu_baseline(wl, args.cpu_budget)
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_budget, dynamic=args.workload == "w8a8_dynamic")
         cpu["gpu_over_cpu"] = value / cpu["value"] if cpu["unit"] == unit else None
 
     line = {

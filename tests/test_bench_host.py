@@ -21,11 +21,13 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-@pytest.mark.parametrize("wid, unit", [(1, "TFLOP/s"), (2, "GB/s")])
-def test_cpu_baseline_fields(wid, unit):
+@pytest.mark.parametrize("wid, unit, dynamic", [(1, "TFLOP/s", False), (2, "GB/s", False), (5, "TOP/s", False),
+                                                (5, "TOP/s", True)])
+def test_cpu_baseline_fields(wid, unit, dynamic):
     wl = synth.WORKLOADS[wid]
-    cb = bench.cpu_baseline(wl, 0.2)
+    cb = bench.cpu_baseline(wl, 0.2, dynamic=dynamic)
     assert cb["kind"] == "oracle" and cb["unit"] == unit
+    assert ("quantiser" in cb["sample"]) == dynamic
     assert cb["value"] > 0 and cb["cores"] >= 1
     assert isinstance(cb["cpu_model"], str) and cb["cpu_model"]
     assert f"of {wl.m} token rows" in cb["sample"]
