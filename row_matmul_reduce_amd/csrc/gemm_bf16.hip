@@ -36,10 +36,10 @@ struct Bf16Op {
     __device__ static __forceinline__ void mfma_acc(Acc &c, Frag a, Frag b) {
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
-    __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const {
-        u32x2 p = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        st8(out + (int64_t)mrow * n + ncol, p);
-    }
+    __device__ static __forceinline__ u32x2 pack(Acc v) { return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
+    __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const { st8(out + (int64_t)mrow * n + ncol, pack(v)); }
+    // 8 consecutive output columns
+    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16(out + (int64_t)mrow * n + ncol, v); }
 };
 
 template <int BN, int PF, bool KTAIL>
