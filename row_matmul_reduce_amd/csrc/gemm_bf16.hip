@@ -40,6 +40,7 @@ struct Bf16Op {
     __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const { st8(out + (int64_t)mrow * n + ncol, pack(v)); }
     // 8 consecutive output columns
     __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16(out + (int64_t)mrow * n + ncol, v); }
+    __device__ static __forceinline__ bool coalesced_final() { return true; }
 };
 
 template <int BN, int PF, bool KTAIL>

@@ -138,16 +138,17 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 //
 // Op supplies: Frag (16-byte operand) and Acc (4-lane accumulator) types, zero(),
 // mfma_acc(acc, weight_frag, activation_frag), and either store(acc, row, col) of 4
-// consecutive columns, pack(acc) of them as 8 output bytes and store16(row, col, v) of 8
-// consecutive output columns (STAGED = false) or, with STAGED = true, stage(rows, cols,
-// m0, n0, wave, lane), which DMAs a value per tile row and per tile column into LDS, and
-// store_staged(acc, row, col, row_value, column_values).
+// consecutive columns and pack(acc) of them as 8 output bytes (STAGED = false) or, with
+// STAGED = true, stage(rows, cols, m0, n0, wave, lane), which DMAs a value per tile row
+// and per tile column into LDS, store_staged(acc, row, col, row_value, column_values) and
+// pack_staged(acc, row_value, column_values); and store16(row, col, v) of 8 consecutive
+// output columns and coalesced_final(), whether the last tile may take the path below.
 //
-// The workgroup's last tile (the only one on shares with one tile per CU) is stored by
-// unstaged Ops through LDS, which no K step needs any more: each lane writes its 4-column
-// pieces into a row-major copy of the tile, then the workgroup stores whole rows with 16
-// bytes per lane, so every store instruction covers full 128-byte lines instead of 32-byte
-// pieces of 16 rows (prefill share: 202.7 -> 199.5 us in a probe of the same engine, with
+// The workgroup's last tile (the only one on shares with one tile per CU) is stored
+// through LDS, which no K step needs any more: each lane writes its 4-column pieces into
+// a row-major copy of the tile, then the workgroup stores whole rows with 16 bytes per
+// lane, so every store instruction covers full 128-byte lines instead of 32-byte pieces
+// of 16 rows (bf16 prefill share: 202.7 -> 199.5 us in a probe of the same engine, with
 // the store itself about 10 us of the kernel).  Tiles that have a successor keep the direct
 // store, which overlaps the successor's first DMAs.
 // smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
@@ -360,8 +361,8 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         have_prev = true;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
-    if constexpr (Op::STAGED) {
-        if (have_prev) store_tile(pm0, pn0, par);
+    if (have_prev && !op.coalesced_final()) {
+        store_tile(pm0, pn0, par);
     } else if (have_prev) {  // uniform over the workgroup
         constexpr int ROWB = BN * 2 + 16;  // tile row in LDS, padded so that 16 rows fall on distinct banks
         constexpr int CPR = BN / 8;        // 16-byte chunks per tile row
@@ -370,13 +371,19 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
 #pragma unroll
         for (int i = LAST + 1; i < NM; ++i) asm volatile("" : "+a"(acc[i / FN][i % FN]));
+        const float *srow = stage_area + par * STAGE_FLOATS, *scol = srow + BM;  // staged Ops only
         __syncthreads();  // every wave's DMAs have landed and its fragment reads are done
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
                 const int r = wm0 + a * 16 + frow, c = wn0 + b * 16 + fchunk * 4;
-                *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = Op::pack(acc[a][b]);
+                u32x2 v;
+                if constexpr (Op::STAGED)
+                    v = op.pack_staged(acc[a][b], srow[r], *reinterpret_cast<const f32x4 *>(scol + c));
+                else
+                    v = Op::pack(acc[a][b]);
+                *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = v;
             }
         __syncthreads();
         for (int i = tid; i < BM * CPR; i += NW * 64) {

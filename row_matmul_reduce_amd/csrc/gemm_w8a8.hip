@@ -35,17 +35,23 @@ struct W8a8Op {
     // Dequantise and store 4 consecutive columns of one row, given that row's token scale
     // s (staged; 0 for pad rows, which read out of range) and the 4 channel scales w, in
     // the order of the definition (no fused multiply-add).
-    __device__ __forceinline__ void store_staged(Acc v, int mrow, int ncol, float s, f32x4 w) const {
+    __device__ __forceinline__ u32x2 pack_staged(Acc v, float s, f32x4 w) const {
         float d[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const float a = (float)v[t];             // v_cvt_f32_i32: nearest-even
             d[t] = __fmul_rn(__fmul_rn(a, s), w[t]);
         }
-        u32x2 p = {pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
-        st8(out + (int64_t)mrow * n + ncol, p);
+        return u32x2{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
+    }
+    __device__ __forceinline__ void store_staged(Acc v, int mrow, int ncol, float s, f32x4 w) const {
+        st8(out + (int64_t)mrow * n + ncol, pack_staged(v, s, w));
         if (acc_out) st16(acc_out + (int64_t)mrow * n + ncol, __builtin_bit_cast(u32x4, v));
     }
+    // 8 consecutive bf16 output columns
+    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16(out + (int64_t)mrow * n + ncol, v); }
+    // the last tile goes through LDS unless the int32 accumulators are stored as well
+    __device__ __forceinline__ bool coalesced_final() const { return acc_out == nullptr; }
     // DMA the token scales of tile rows m0 .. m0+255 (wave 0) and the channel scales of
     // columns n0 .. n0+255 (wave 1) into LDS; entries past m or n read as zero.
     __device__ __forceinline__ void stage(float *rows, float *cols, int m0, int n0, int wave, int lane) const {

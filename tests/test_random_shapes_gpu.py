@@ -57,6 +57,9 @@ def test_random_w8a8_partial(m, n, k, tp):
     wout, wacc = oracle.w8a8_rows(xq, sx, wq, sw, m, tp=tp)
     assert np.array_equal(acc.cpu().numpy(), wacc), "int32 accumulators must be bit-exact"
     assert np.array_equal(host_bf16(out), wout), "dequantised output (same fp32 operation order)"
+    # without the accumulator store (the last tile then goes out through LDS) the bits are the same
+    out2 = rpl.rpl_w8a8_partial(dev(xq), dev(sx), dev(wq), dev(sw), tp)
+    assert np.array_equal(host_bf16(out2), wout), "dequantised output without the accumulator store"
 
 
 @pytest.mark.parametrize("m,n,k,tp", _shapes(2026, 8, 8))
