@@ -144,19 +144,22 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 // pack_staged(acc, row_value, column_values); and store16(row, col, v) of 8 consecutive
 // output columns and coalesced_final(), whether the last tile may take the path below.
 //
-// The workgroup's last tile (the only one on shares with one tile per CU) is stored
-// through LDS, which no K step needs any more: each lane writes its 4-column pieces into
-// a row-major copy of the tile, then the workgroup stores whole rows with 16 bytes per
-// lane, so every store instruction covers full 128-byte lines instead of 32-byte pieces
-// of 16 rows (bf16 prefill share: 202.7 -> 199.5 us in a probe of the same engine, with
-// the store itself about 10 us of the kernel).  Tiles that have a successor keep the direct
-// store, which overlaps the successor's first DMAs.
+// Finished tiles are stored through LDS: each lane writes its 4-column pieces into a
+// row-major copy of the tile, then the workgroup stores whole rows with 16 bytes per lane,
+// so every store instruction covers full 128-byte lines instead of 32-byte pieces of 16
+// rows.  The last tile of a workgroup (the only one on shares with one tile per CU) is
+// stored after the K loop (bf16 prefill share: 202.7 -> 199.5 us in a probe of the same
+// engine, the store itself being about 10 us of the kernel); a tile with a successor is
+// stored before the successor's first DMAs, since its copy needs the operand buffers
+// (long-prefill share: 429.1 -> 417.9 us against the direct store overlapped with those
+// DMAs).  Staged Ops take this path only for the last tile and only when coalesced_final()
+// (a second copy of it pushes the int8 kernel's registers into spills).
 // smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
 // staged Op.  KTAIL: K is not a whole number of steps (kbytes % KT_BYTES != 0), so the
 // last step's chunks past K are cut lane by lane; without a tail only whole steps past
 // the end are cut, by one uniform test per step, and the DMA addressing needs no
 // vector instruction at all (2-3% faster on the prefill shares than the per-lane form).
-template <int BN, int PF, bool KTAIL, class Op>
+template <int BN, int PF, bool KTAIL, class Op, bool CO_LOOP = true>
 __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, uint8_t *smem) {
     constexpr int BM = 256, NW = 4, WN = 2;
     constexpr int TM = BM / 2, TN = BN / WN;
@@ -313,6 +316,42 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         }
     };
 
+    // A finished tile through LDS (no K step may be in flight): each lane writes its 4-column
+    // pieces into a row-major copy of the tile, then the workgroup stores whole rows, 16 bytes
+    // per lane.  Ends with the LDS free again.
+    auto store_tile_lds = [&](int m0, int n0, int p) {
+        constexpr int ROWB = BN * 2 + 16;  // tile row in LDS, padded so that 16 rows fall on distinct banks
+        constexpr int CPR = BN / 8;        // 16-byte chunks per tile row
+        static_assert(BM * ROWB <= 2 * BUF, "the tile fits the operand buffers");
+        constexpr int LAST = (NR - 1) * NM / NR;
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
+#pragma unroll
+        for (int i = LAST + 1; i < NM; ++i) asm volatile("" : "+a"(acc[i / FN][i % FN]));
+        const float *srow = stage_area + p * STAGE_FLOATS, *scol = srow + BM;  // staged Ops only
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last steps' out-of-range DMAs into LDS
+        __syncthreads();  // every wave's DMAs have landed and its fragment reads are done
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) {
+                const int r = wm0 + a * 16 + frow, c = wn0 + b * 16 + fchunk * 4;
+                u32x2 v;
+                if constexpr (Op::STAGED)
+                    v = op.pack_staged(acc[a][b], srow[r], *reinterpret_cast<const f32x4 *>(scol + c));
+                else
+                    v = Op::pack(acc[a][b]);
+                *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = v;
+            }
+        __syncthreads();
+        for (int i = tid; i < BM * CPR; i += NW * 64) {
+            const int r = i / CPR, c = i - r * CPR;
+            if (m0 + r < g.m_pad && n0 + c * 8 < g.n)
+                op.store16(m0 + r, n0 + c * 8, *reinterpret_cast<const u32x4 *>(smem + r * ROWB + c * 16));
+        }
+        __syncthreads();  // every wave's reads of the copy have returned before LDS is reused
+    };
+    const bool co = op.coalesced_final();  // uniform: a kernel argument
+
     int pm0 = 0, pn0 = 0, par = 0;
     bool have_prev = false;
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
@@ -324,14 +363,21 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         rx = span_rsrc(sx, true);
         rw = span_rsrc(sw, true);
         pfx0 = (tn % PF_SHARE_X) * (BM / PF_SHARE_X);
+        // (staged Ops keep the direct store between tiles: the second copy of the LDS path
+        // pushes the int8 kernel's registers into spills)
+        const bool lds_store = CO_LOOP && !Op::STAGED && co && have_prev;  // uniform
+        if (lds_store) {  // the previous tile goes out first, through LDS
+            store_tile_lds(pm0, pn0, par);
+            par = 1 - par;
+        }
         if constexpr (Op::STAGED) {
-            float *srow = stage_area + (have_prev ? 1 - par : par) * STAGE_FLOATS;
+            float *srow = stage_area + (have_prev && !lds_store ? 1 - par : par) * STAGE_FLOATS;
             op.stage(srow, srow + BM, m0, n0, wave, lane);  // lands before this prologue's barrier
         }
         for (int d = 2; d < PF; ++d) prefetch(d);
 #pragma unroll
         for (int j = 0; j < NR; ++j) dma(0, s0, j);  // the previous tile's reads all ended at its barriers
-        if (have_prev) {
+        if (have_prev && !lds_store) {
             store_tile(pm0, pn0, par);
             par = 1 - par;
         }
@@ -361,36 +407,9 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         have_prev = true;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write in flight when the workgroup retires
-    if (have_prev && !op.coalesced_final()) {
-        store_tile(pm0, pn0, par);
-    } else if (have_prev) {  // uniform over the workgroup
-        constexpr int ROWB = BN * 2 + 16;  // tile row in LDS, padded so that 16 rows fall on distinct banks
-        constexpr int CPR = BN / 8;        // 16-byte chunks per tile row
-        static_assert(BM * ROWB <= 2 * BUF, "the tile fits the operand buffers");
-        constexpr int LAST = (NR - 1) * NM / NR;
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
-#pragma unroll
-        for (int i = LAST + 1; i < NM; ++i) asm volatile("" : "+a"(acc[i / FN][i % FN]));
-        const float *srow = stage_area + par * STAGE_FLOATS, *scol = srow + BM;  // staged Ops only
-        __syncthreads();  // every wave's DMAs have landed and its fragment reads are done
-#pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int r = wm0 + a * 16 + frow, c = wn0 + b * 16 + fchunk * 4;
-                u32x2 v;
-                if constexpr (Op::STAGED)
-                    v = op.pack_staged(acc[a][b], srow[r], *reinterpret_cast<const f32x4 *>(scol + c));
-                else
-                    v = Op::pack(acc[a][b]);
-                *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = v;
-            }
-        __syncthreads();
-        for (int i = tid; i < BM * CPR; i += NW * 64) {
-            const int r = i / CPR, c = i - r * CPR;
-            if (pm0 + r < g.m_pad && pn0 + c * 8 < g.n)
-                op.store16(pm0 + r, pn0 + c * 8, *reinterpret_cast<const u32x4 *>(smem + r * ROWB + c * 16));
-        }
+    if (have_prev) {  // uniform over the workgroup
+        if (co) store_tile_lds(pm0, pn0, par);
+        else store_tile(pm0, pn0, par);
     }
 }
 
