@@ -263,7 +263,9 @@ rpl_status rpl_rmsnorm_slice_apply(const float *h, const float *const *sumsq_par
  *   x_scale[r] = amax[r] / 127                       (IEEE division, nearest-even)
  *   xq[r, k]   = clamp(rint(x[r, k] / x_scale[r]), -127, 127)
  * rint rounds half to even; an all-zero row gets x_scale 0 and all codes 0.
- * Codes are exact functions of the input (correctly rounded divisions).  Inputs
+ * Every code equals the one from the correctly rounded quotient x / x_scale,
+ * so codes are exact functions of the input (the kernel may form the quotient
+ * another way where that cannot change a code).  Inputs
  * must be finite: a row holding Inf or NaN gets unspecified codes and scale.
  *
  * x        [m, k] bf16, row stride ldx >= k
