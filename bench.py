@@ -308,7 +308,9 @@ class Path:
 def fused_decode(torch, rpl, copies: int, all_rows: bool, launches: int = 200):
     """The single-launch decode path (every shard's product + sum + residual + RMSNorm) on the
     decode o_proj workload: rank 0's token chunk (reduce-scatter form) or all rows (all-reduce
-    form).  Timed by replaying a HIP graph of `launches` launches over rotated weight copies."""
+    form).  Timed by replaying a HIP graph of `launches` launches over rotated weight copies,
+    next to the unfused composition on the same inputs (a bf16 partial per shard, then the
+    reduce + RMSNorm), captured and replayed the same way, in alternating replays."""
     from row_matmul_reduce_amd import synth
     wl = synth.WORKLOADS[WORKLOAD_IDS["decode"]]
     rows = wl.m if all_rows else wl.m_chunk
@@ -324,29 +326,77 @@ def fused_decode(torch, rpl, copies: int, all_rows: bool, launches: int = 200):
     if copies <= 0:
         copies = max(3, -(-(2 * MALL_BYTES + 1) // set_bytes) + 1)
     sets = [ws] + [[t.clone() for t in ws] for _ in range(copies - 1)]
-    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(rows, wl.n)
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(rows, wl.n, wl.tp)
     y = torch.empty_like(res)
     ro = torch.empty_like(res)
-    for i in range(len(sets)):
-        rpl.rpl_matmul_reduce_rmsnorm(xs, sets[i], res, gam, wl.eps, workspace=work, y=y, residual_out=ro)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(launches):
-            rpl.rpl_matmul_reduce_rmsnorm(xs, sets[i % len(sets)], res, gam, wl.eps, workspace=work, y=y,
-                                          residual_out=ro)
-    g.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / launches
+    parts = [torch.empty((rows, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(wl.tp)]
+    y2, ro2 = torch.empty_like(res), torch.empty_like(res)
+
+    def fused(i):
+        rpl.rpl_matmul_reduce_rmsnorm(xs, sets[i % len(sets)], res, gam, wl.eps, workspace=work, y=y,
+                                      residual_out=ro)
+
+    def unfused(i):
+        for s in range(wl.tp):
+            rpl.rpl_partial(xs[s], sets[i % len(sets)][s], 1, out=parts[s])
+        rpl.rpl_reduce_chunk_rmsnorm(parts, res, gam, wl.eps, y=y2, residual_out=ro2)
+
+    def capture(fn):
+        for i in range(len(sets)):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_us(g):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / launches
+
+    gf, gu = capture(fused), capture(unfused)
+    tf, tu = [], []
+    for _ in range(5):
+        tf.append(replay_us(gf))
+        tu.append(replay_us(gu))
+    us, uus = float(np.median(tf)), float(np.median(tu))
+    status = rpl.rpl_matmul_reduce_rmsnorm_status(work)
     nbytes = (wl.tp * wl.n * wl.k_shard * 2 + wl.tp * rows * wl.k_shard * 2 + 3 * rows * wl.n * 2 + wl.n * 2)
     return {"workload": wl.name, "rows": rows, "form": "all-reduce" if all_rows else "reduce-scatter chunk",
             "shards": wl.tp, "us": us, "bytes": nbytes, "GB/s": nbytes / (us * 1e-6) / 1e9,
-            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "weight_sets_rotated": len(sets)}
+            "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "weight_sets_rotated": len(sets),
+            "unfused_us": uus, "fused_over_unfused_time": us / uus,
+            "unfused_what": f"rpl_partial per shard ({rows} rows each) + rpl_reduce_chunk_rmsnorm, same inputs, "
+                            f"same graph replay; medians of 5 alternating replays of {launches} launches each",
+            "workspace_status": status}
+
+
+def plain_read_ceiling(torch, rpl, tensors, launches: int = 200):
+    """What a standalone launch that only reads one of `tensors` achieves here, timed like the
+    decode kernels (HIP graph of `launches` launches over the rotated copies): the library's
+    plain streaming read (rpl_read_ceiling, measurement only) at several grid sizes, the best
+    of them as the ceiling; torch's own row reduction of the same copies as context."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grids = {}
+    for grid in (224, 256, 512, 1024, 2048, 4096):
+        grids[grid] = _graph_mean_us(torch, lambda i, g=grid: rpl.rpl_read_ceiling(tensors[i % len(tensors)], g, sink),
+                                     len(tensors), launches)
+    best = min(grids, key=grids.get)
+    t_sum = _graph_mean_us(torch, lambda i: torch.sum(tensors[i % len(tensors)], dim=1, dtype=torch.float32),
+                           len(tensors), launches)
+    nbytes = tensors[0].numel() * tensors[0].element_size()
+    return {"what": "rpl_read_ceiling (a plain grid-stride read that writes nothing) of one rotated weight copy "
+                    "per launch, HIP graph replay, best grid", "grid": best, "us": grids[best], "bytes": nbytes,
+            "GB/s": nbytes / (grids[best] * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (grids[best] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "us_by_grid": grids, "torch_row_sum_us": t_sum}
 
 
 def _graph_mean_us(torch, fn, n_sets: int, launches: int = 100):
@@ -712,6 +762,11 @@ def main():
                 s_ms, s_kern, s_period = sp.run(10, 3)
             side[key] = {"workload": swl.name, "ms_per_step": s_ms, "input_sets_rotated": len(sp.sets),
                          "kernels": sp.kernels_report(s_kern, s_period)}
+            if swl.m_pad <= 16:  # decode: the same weight copies read by a plain standalone launch
+                ceil = plain_read_ceiling(torch, rpl, [d["w"] for d in sp.sets])
+                kp = side[key]["kernels"][sp.pname]
+                kp["plain_read_ceiling"] = ceil
+                kp["frac_of_ceiling"] = ceil["us"] / kp["us"]
             if key == "long_prefill":
                 side[key]["library_reference"] = library_reference(sp, torch)
             del sp

@@ -306,10 +306,18 @@ rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx,
  * w_shards   HOST array of tp DEVICE pointers, each -> [n, k] bf16, stride ldw >= k
  * residual   [m, n] bf16 contiguous; residual_out [m, n] bf16 (may be exactly
  *            residual); y [m, n] bf16; gamma [n] bf16; eps >= 0, finite
- * workspace  device buffer of at least rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
- *            bytes, 256-byte aligned.  Its first 4 bytes must be zero before its
- *            first use; every call leaves them zero again.  Calls that share a
- *            workspace must not run concurrently (same stream is fine).
+ * workspace  device buffer of at least
+ *            rpl_matmul_reduce_rmsnorm_workspace_size(m, n, tp) bytes, 256-byte
+ *            aligned, ZERO-FILLED before its first use; a call leaves it ready
+ *            for the next one (nothing to reset).  It carries the shards'
+ *            rounded products from the launch's product workgroups to its
+ *            row workgroups, one call count per workgroup and, at byte offset 8, a 32-bit
+ *            status word: 0, or nonzero once a workgroup of some call waited
+ *            past its bound for another (the launch is cooperative, so every
+ *            workgroup is resident and this does not happen in a correct launch;
+ *            that call's y is then NaN).  The word at byte offset 12 bounds the
+ *            waits in polls (0 = the default, about 2^22).  Calls that share a
+ *            workspace must not overlap in time (same stream is fine).
  * y, residual_out and workspace must not overlap inputs or each other (except
  * residual_out == residual).
  *
@@ -318,12 +326,17 @@ rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx,
  * RPL_ERR_INVALID     m < 0, m_valid < 0 or > m, n < 1, k < 1, tp < 1, ldx < k,
  *                     ldw < k, eps < 0 or not finite, workspace too small,
  *                     overlaps
- * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; m > 64; n, k, ldx or ldw not a multiple
- *                     of 8; bf16 pointers not 16-byte aligned, workspace not
- *                     256-byte aligned; n or k >= 2^31
- * RPL_ERR_LAUNCH      the kernel launch failed
+ * RPL_ERR_UNSUPPORTED tp > RPL_MAX_TP; m > 64; n > 8192; n, k, ldx or ldw not a
+ *                     multiple of 8; bf16 pointers not 16-byte aligned, workspace
+ *                     not 256-byte aligned; k >= 2^31
+ * RPL_ERR_LAUNCH      the kernel launch failed, or the device cannot hold the
+ *                     m row workgroups and one product workgroup at once
+ *
+ * rpl_matmul_reduce_rmsnorm_workspace_size returns the bytes for m rows, n
+ * columns and tp shards (4 * m * tp * n plus a 4352-byte header), or -1
+ * outside 0 <= m <= 64, 1 <= n <= 8192, 1 <= tp <= RPL_MAX_TP.
  */
-int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n);
+int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n, int32_t tp);
 
 rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx,
                                      const rpl_bf16 *const *w_shards, int64_t ldw,
@@ -372,7 +385,7 @@ rpl_status rpl_gather_rows(const rpl_bf16 *const *chunks, int32_t tp, int64_t m_
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 1.4. */
+/* Library ABI version: (major << 16) | minor.  Currently 2.0. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

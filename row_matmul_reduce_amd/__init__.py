@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
         L.rpl_w8a8_partial.restype = ctypes.c_int
         L.rpl_w8a8_partial.argtypes = [_p, _i64, _p, _p, _i64, _p, _p, _p, _i64, _i64, _i64, _i32, _p]
         L.rpl_matmul_reduce_rmsnorm_workspace_size.restype = _i64
-        L.rpl_matmul_reduce_rmsnorm_workspace_size.argtypes = [_i64, _i64]
+        L.rpl_matmul_reduce_rmsnorm_workspace_size.argtypes = [_i64, _i64, _i32]
         L.rpl_matmul_reduce_rmsnorm.restype = ctypes.c_int
         L.rpl_matmul_reduce_rmsnorm.argtypes = [_p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _p,
                                                 ctypes.c_float, _p, _p, _p, _i64, _p]
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.rpl_shard_rows.argtypes = [_p, _i64, _i64, _i64, _i32, _i32, _p, _p]
         L.rpl_gather_rows.restype = ctypes.c_int
         L.rpl_gather_rows.argtypes = [_p, _i32, _i64, _i64, _i64, _i64, _p, _p]
+        L.rpl_read_ceiling.restype = ctypes.c_int
+        L.rpl_read_ceiling.argtypes = [_p, _i64, _i32, _p, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
         L.rpl_status_string.argtypes = [ctypes.c_int]
         L.rpl_version.restype = ctypes.c_int32
@@ -351,13 +353,25 @@ def rpl_rmsnorm_slice_apply(h, sumsq_parts, n_total: int, gamma, eps: float, y, 
     return y
 
 
-def rpl_matmul_reduce_rmsnorm_workspace(m: int, n: int, device=None):
-    """A zero-filled workspace for rpl_matmul_reduce_rmsnorm on [m, n] (reusable across calls)."""
+def rpl_matmul_reduce_rmsnorm_workspace(m: int, n: int, tp: int, device=None):
+    """A zero-filled workspace for rpl_matmul_reduce_rmsnorm on [m, n] with tp shards (reusable
+    across calls, which leave it ready for the next one)."""
     torch = _torch()
-    size = lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
+    size = lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n, tp)
     if size < 0:
-        raise ValueError(f"unsupported shape m={m} n={n} for rpl_matmul_reduce_rmsnorm")
-    return torch.zeros(max(size, 1), dtype=torch.uint8, device=device or "cuda")
+        raise ValueError(f"unsupported shape m={m} n={n} tp={tp} for rpl_matmul_reduce_rmsnorm")
+    return torch.zeros(max(size, 16), dtype=torch.uint8, device=device or "cuda")
+
+
+def rpl_matmul_reduce_rmsnorm_status(workspace) -> int:
+    """The workspace's status word (synchronises): 0, or nonzero once a call's workgroup waited past
+    its bound for another (that call's y is NaN)."""
+    return int(workspace[8:12].view(_torch().int32).item())
+
+
+def rpl_matmul_reduce_rmsnorm_set_poll_bound(workspace, polls: int):
+    """Bound, in polls, on every wait of the calls that use this workspace (0 = the default)."""
+    workspace[12:16].view(_torch().int32).fill_(int(polls))
 
 
 def rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps: float, workspace=None, y=None,
@@ -393,7 +407,7 @@ def rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps: float, w
     if residual_out is None:
         residual_out = torch.empty_like(residual)
     if workspace is None:
-        workspace = rpl_matmul_reduce_rmsnorm_workspace(m, n, residual.device)
+        workspace = rpl_matmul_reduce_rmsnorm_workspace(m, n, tp, residual.device)
     xs = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in x_shards])
     ws = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in w_shards])
     st = lib().rpl_matmul_reduce_rmsnorm(ctypes.cast(xs, _p), ldx, ctypes.cast(ws, _p), ldw, tp, m, m_valid, n, k,
@@ -404,8 +418,19 @@ def rpl_matmul_reduce_rmsnorm(x_shards, w_shards, residual, gamma, eps: float, w
     return y, residual_out
 
 
+def rpl_read_ceiling(t, grid: int, sink, stream=None):
+    """Measurement only: read every byte of device tensor t once with `grid` workgroups (a plain
+    streaming read that writes nothing; sink is a device int32 tensor of at least one element)."""
+    if not t.is_cuda or not sink.is_cuda or not t.is_contiguous():
+        raise ValueError("device tensors, t contiguous")
+    st = lib().rpl_read_ceiling(t.data_ptr(), t.numel() * t.element_size(), int(grid), sink.data_ptr(),
+                                _stream(t, stream))
+    _check("rpl_read_ceiling", st)
+
+
 __all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
-           "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace", "rpl_sum_partials",
+           "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace", "rpl_matmul_reduce_rmsnorm_status",
+           "rpl_matmul_reduce_rmsnorm_set_poll_bound", "rpl_sum_partials",
            "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
-           "rpl_status_string", "rpl_version",
+           "rpl_status_string", "rpl_version", "rpl_read_ceiling",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

@@ -55,16 +55,6 @@ gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
 constexpr int DEC_WAVES = 4;
 constexpr int DEC_BATCH = 16;  // K steps (32 values each) whose loads are issued together
 
-// Lane i of the result takes lane i + SH of v within each row of 16 lanes (zero past the row).
-template <int SH>
-__device__ __forceinline__ u32x4 lanes_down(u32x4 v) {
-    static_assert(SH > 0 && SH < 16, "a row shift");
-    u32x4 r;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_update_dpp(0u, v[q], 0x100 + SH, 0xF, 0xF, true);
-    return r;
-}
-
 // XP: K steps per activation load.  The MFMA takes token row r from lanes r, r+16, r+32,
 // r+48; with m_pad <= 16/XP rows the other lanes of a load would be idle, so lane row
 // r16 loads token row r16 % (16/XP) of step s + r16 / (16/XP), and step s + q reads its

@@ -275,9 +275,9 @@ rpl_status rpl_quant_per_token(const rpl_bf16 *x, int64_t ldx, int8_t *xq, int64
                                                      static_cast<hipStream_t>(stream)));
 }
 
-int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n) {
-    if (m < 0 || n < 1 || m > 64 || n > kMaxDim) return -1;
-    return rpl::fused_decode_workspace_bytes(m, n);
+int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n, int32_t tp) {
+    if (m < 0 || n < 1 || tp < 1 || m > 64 || n > rpl::FD_MAX_N || tp > RPL_MAX_TP) return -1;
+    return rpl::fused_decode_workspace_bytes(m, n, tp);
 }
 
 rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx, const rpl_bf16 *const *w_shards,
@@ -298,7 +298,7 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
     const int np = tp <= RPL_MAX_TP ? tp : 0;
     const int64_t mat = span(m, n, n, 2), gb = span(1, n, n, 2);
     const int64_t xb = span(m_valid, k, ldx, 2), wb = span(n, k, ldw, 2);
-    const int64_t need = (m <= 64 && n <= kMaxDim) ? rpl::fused_decode_workspace_bytes(m, n) : 0;
+    const int64_t need = (m <= 64 && n <= rpl::FD_MAX_N && np) ? rpl::fused_decode_workspace_bytes(m, n, tp) : 0;
     if (m != 0 && workspace_bytes < need) return RPL_ERR_INVALID;
     const int64_t wsb = workspace_bytes < 0 ? 0 : workspace_bytes;
     // outputs and workspace against the inputs and each other
@@ -314,13 +314,14 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
         for (int q = o + 1; q < 3; ++q)
             if (overlap(outs[o], osz[o], outs[q], osz[q])) return RPL_ERR_INVALID;
     }
-    if (tp > RPL_MAX_TP || m > 64 || n % 8 || k % 8 || ldx % 8 || ldw % 8) return RPL_ERR_UNSUPPORTED;
+    if (tp > RPL_MAX_TP || m > 64 || n > rpl::FD_MAX_N || n % 8 || k % 8 || ldx % 8 || ldw % 8)
+        return RPL_ERR_UNSUPPORTED;
     if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(y, 16) || !aligned(residual_out, 16) ||
         !aligned(workspace, 256))
         return RPL_ERR_UNSUPPORTED;
     for (int s = 0; s < tp; ++s)
         if (!aligned(w_shards[s], 16) || !aligned(x_shards[s], 16)) return RPL_ERR_UNSUPPORTED;
-    if (n > kMaxDim || k > kMaxDim) return RPL_ERR_UNSUPPORTED;
+    if (k > kMaxDim) return RPL_ERR_UNSUPPORTED;
     if (m == 0) return RPL_OK;
     rpl::FusedDecodeArgs a{};
     for (int s = 0; s < tp; ++s) {
@@ -340,9 +341,10 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
     a.y = y;
     a.residual_out = residual_out;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    a.counter = reinterpret_cast<unsigned *>(ws);
-    a.ss_ws = reinterpret_cast<float *>(ws + rpl::FD_WS_HEADER);
-    a.h_ws = reinterpret_cast<float *>(ws + rpl::FD_WS_HEADER + rpl::fused_decode_ss_bytes(m, n));
+    a.calls = reinterpret_cast<unsigned *>(ws + 256);
+    a.status = reinterpret_cast<unsigned *>(ws + 8);
+    a.poll_limit = reinterpret_cast<const unsigned *>(ws + 12);
+    a.p_slots = reinterpret_cast<unsigned long long *>(ws + rpl::FD_WS_HEADER);
     return launch_status(rpl::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -357,6 +359,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (1 << 16) | 4; }
+int32_t rpl_version(void) { return (2 << 16) | 0; }
 
 }  // extern "C"

@@ -35,4 +35,15 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 *>(p) = v; }
 
+// Lane i of the result takes lane i + SH of v within each row of 16 lanes (zero past the
+// row): a DPP row shift, which moves an MFMA operand fragment between token-row lanes.
+template <int SH>
+__device__ __forceinline__ u32x4 lanes_down(u32x4 v) {
+    static_assert(SH > 0 && SH < 16, "a row shift");
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_update_dpp(0u, v[q], 0x100 + SH, 0xF, 0xF, true);
+    return r;
+}
+
 }  // namespace rpl

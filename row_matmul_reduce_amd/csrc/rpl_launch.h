@@ -27,10 +27,13 @@ hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int 
                                  const uint16_t *gamma, float eps, uint16_t *y, uint16_t *residual_out,
                                  hipStream_t st);
 
-// The single-launch decode path (decode_fused.hip).  Workspace layout: a 256-byte
-// header whose first word is the completion counter, then the per-row partial sums of
-// squares [m][nblk] fp32 (padded to 256 bytes), then h [m][n] fp32.
-constexpr int64_t FD_WS_HEADER = 256;
+// The single-launch decode path (decode_fused.hip).  Workspace: a FD_WS_HEADER-byte header
+// (bytes 8..11 the status word, 12..15 the poll bound, from 256 one 32-bit call count per
+// workgroup), then the tagged hand-off slots, 8 bytes for two bf16 products each: [m][tp][n/2].
+// The whole workspace is zero before its first use.
+constexpr int FD_MAX_GRID = 1024;   // most workgroups of one launch (all resident at once)
+constexpr int64_t FD_WS_HEADER = 256 + 4 * FD_MAX_GRID;
+constexpr int64_t FD_MAX_N = 8192;  // row width one epilogue workgroup holds in registers
 struct FusedDecodeArgs {
     const uint16_t *x[MAX_TP];  // per shard: [m_valid, k] rows, stride ldx
     const uint16_t *w[MAX_TP];  // per shard: [n, k], stride ldw
@@ -39,11 +42,12 @@ struct FusedDecodeArgs {
     const uint16_t *residual, *gamma;
     float eps;
     uint16_t *y, *residual_out;
-    float *ss_ws, *h_ws;
-    unsigned *counter;
+    unsigned *calls;                  // header bytes 256..: one call count per workgroup
+    unsigned *status;                 // header bytes 8..11
+    const unsigned *poll_limit;       // header bytes 12..15
+    unsigned long long *p_slots;      // [m][tp][n / 2]
 };
-int64_t fused_decode_workspace_bytes(int64_t m, int64_t n);
-int64_t fused_decode_ss_bytes(int64_t m, int64_t n);
+int64_t fused_decode_workspace_bytes(int64_t m, int64_t n, int64_t tp);
 hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st);
 
 hipError_t launch_sum_partials(const PartialPtrs &p, int tp, int m, int n, int64_t ldp, uint16_t *out,

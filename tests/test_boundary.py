@@ -8,6 +8,7 @@ are host memory standing in for device memory: a rejected call must not
 touch them.  No call in this file reaches a kernel launch.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -18,18 +19,21 @@ import row_matmul_reduce_amd as rpl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rpl.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, NULL, INVALID, UNSUP = rpl.RPL_OK, rpl.RPL_ERR_NULL, rpl.RPL_ERR_INVALID, rpl.RPL_ERR_UNSUPPORTED
 
 
-def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rpl_[a-z0-9_]+)\s*\(", src)))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(rpl_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_path_calls():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for f in ("rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
               "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace_size",
               "rpl_sum_partials", "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
@@ -40,7 +44,7 @@ def test_header_declares_the_path_calls():
 def test_library_exports_every_declared_symbol():
     L = rpl.lib()
     for name in declared_functions():
-        assert hasattr(L, name), f"{name} declared in rpl.h but not exported"
+        assert hasattr(L, name), f"{name} declared in include/ but not exported"
     # and exports no other rpl_ function (nm on the built object)
     import subprocess
     out = subprocess.run(["nm", "-D", "--defined-only", rpl.LIB_PATH], capture_output=True, text=True).stdout
@@ -52,7 +56,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (1 << 16) | 4
+    assert rpl.rpl_version() == (2 << 16) | 0
 
 
 class Buf:
@@ -239,16 +243,22 @@ def fused_call(xs, ldx, ws, ldw, tp, m, mv, n, k, res, gam, eps, y, ro, work, wb
 
 def test_fused_decode_workspace_size():
     L = rpl.lib()
-    # header 256 B + per-row partial sums [m][n/16] fp32 padded to 256 B + h [m][n] fp32
-    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 3584) == 256 + 3584 + 4 * 4 * 3584
-    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(1, 8) == 256 + 256 + 32
-    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(65, 64) == -1
-    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(-1, 64) == -1
+    # header (256 B + a 4-byte call count for each of up to 1024 workgroups), then the 8-byte
+    # slots of two bf16 products each: [m][tp][n/2]
+    hdr = 256 + 4 * 1024
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 3584, 2) == hdr + 4 * 4 * 2 * 3584
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(1, 8, 1) == hdr + 4 * 8
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(64, 8192, 16) == hdr + 4 * 64 * 16 * 8192
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(65, 64, 2) == -1
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(-1, 64, 2) == -1
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 8200, 2) == -1
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 64, 0) == -1
+    assert L.rpl_matmul_reduce_rmsnorm_workspace_size(4, 64, 17) == -1
 
 
 def test_fused_decode_validation():
     tp, m, n, k = 2, 4, 64, 32
-    wsz = rpl.lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n)
+    wsz = rpl.lib().rpl_matmul_reduce_rmsnorm_workspace_size(m, n, tp)
     X0, X1, W0, W1 = Buf(m * k * 2), Buf(m * k * 2), Buf(n * k * 2), Buf(n * k * 2)
     R, G, Y, RO = Buf(m * n * 2), Buf(n * 2), Buf(m * n * 2), Buf(m * n * 2)
     WS = Buf(wsz + 512)
@@ -275,6 +285,7 @@ def test_fused_decode_validation():
         (dict(ro=r + 16), INVALID),                 # residual_out partially overlaps the residual
         (dict(tp=17, xs=xs * 9, ws=wl * 9), UNSUP), (dict(m=65, mv=4, res=1 << 40, y=1 << 41, ro=1 << 42, work=1 << 43, wbytes=1 << 20), UNSUP),
         (dict(n=60, res=1 << 40, y=1 << 41, ro=1 << 42, work=1 << 43, wbytes=1 << 20), UNSUP), (dict(k=36, ldx=40, ldw=40), UNSUP), (dict(ldx=36), UNSUP),
+        (dict(n=8200, res=1 << 40, y=1 << 41, ro=1 << 42, work=1 << 43, wbytes=1 << 30), UNSUP),  # n > 8192
         (dict(xs=[X0.ptr + 8, X1.ptr]), UNSUP), (dict(work=ws_ptr + 16, wbytes=wsz), UNSUP),
         (dict(y=y + 8), UNSUP),
     ]
@@ -401,3 +412,19 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b|rpl_oracle|\borc_", text, flags=re.M), f
+
+
+def test_read_ceiling_validation():
+    """The measurement helper checks its arguments on the host like the path's calls."""
+    L = rpl.lib()
+    B, S = Buf(4096), Buf(64)
+    call = lambda p, nbytes, grid, sink: L.rpl_read_ceiling(p, nbytes, grid, sink, None)
+    assert call(None, 4096, 256, S.ptr) == NULL
+    assert call(B.ptr, 4096, 256, None) == NULL
+    assert call(B.ptr, 8, 256, S.ptr) == INVALID
+    assert call(B.ptr, 4100, 256, S.ptr) == INVALID
+    assert call(B.ptr, 4096, 0, S.ptr) == INVALID
+    assert call(B.ptr, 4096, 65537, S.ptr) == INVALID
+    assert call(B.ptr + 8, 4080, 256, S.ptr) == UNSUP
+    assert call(B.ptr, 4096, 256, S.ptr + 2) == UNSUP
+    assert B.untouched() and S.untouched()

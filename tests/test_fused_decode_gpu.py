@@ -3,7 +3,7 @@ through the C ABI, against the CPU oracle's unfused composition: a bf16
 partial per shard (oracle.partial_rows), then the sum of the partials,
 residual add and RMSNorm (oracle.reduce_chunk_rmsnorm).  Outputs follow the
 bf16 rule |gpu - oracle| <= 2e-2 + 1e-2 |oracle|; repeated calls on one
-workspace must give identical bits and leave its counter at zero.
+workspace must give identical bits and leave its status word at zero.
 """
 import numpy as np
 import pytest
@@ -45,10 +45,17 @@ def _inputs(m, m_valid, n, k, tp, seed):
     return xs, ws, res, gam
 
 
-# (m, m_valid, n, k, tp): one to four 16-row blocks, padding rows, ragged K steps,
-# one to eight shards, the 910C operator's case (40 rows, hidden 2048, TP=2)
-FUSED_SHAPES = [(1, 1, 8, 8, 1), (4, 4, 264, 1000, 2), (5, 3, 520, 328, 3), (16, 16, 512, 512, 2),
-                (17, 17, 1024, 256, 4), (40, 40, 2048, 1024, 2), (64, 60, 136, 72, 8), (33, 0, 64, 64, 2)]
+# (m, m_valid, n, k, tp): one to four 16-row blocks and every activation packing (1-4, 5-8 and
+# 9-16 rows), padding rows, ragged K steps, one to sixteen shards, rows from 8 to 8192 wide
+# (the epilogue's threads own one to four quads of columns), the 910C operator's case (40 rows,
+# hidden 2048, TP=2), and more
+# (column block, shard) items than the launch has product workgroups, so each computes several
+# (8 x 320 and 2 x 512 items, the widest rows 8192), with a half column block at the end
+# (n % 16 == 8)
+FUSED_SHAPES = [(1, 1, 8, 8, 1), (4, 4, 264, 1000, 2), (5, 3, 520, 328, 3), (12, 12, 200, 1064, 2),
+                (16, 16, 512, 512, 2), (17, 17, 1024, 256, 4), (40, 40, 2048, 1024, 2), (64, 60, 136, 72, 8),
+                (33, 0, 64, 64, 2), (4, 4, 72, 64, 16), (8, 8, 5120, 256, 8), (40, 37, 8192, 96, 2),
+                (3, 3, 4104, 512, 3)]
 
 
 @pytest.mark.parametrize("m,m_valid,n,k,tp", FUSED_SHAPES)
@@ -69,20 +76,74 @@ def test_fused_workspace_reuse_and_in_place():
     m, n, k, tp = 8, 512, 256, 2
     xs, ws, res, gam = _inputs(m, m, n, k, tp, seed=3)
     dx, dw, dg = [dev_bf16(x) for x in xs], [dev_bf16(w) for w in ws], dev_bf16(gam)
-    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(m, n)
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(m, n, tp)
     outs = []
     for _ in range(3):
         y, ro = rpl.rpl_matmul_reduce_rmsnorm(dx, dw, dev_bf16(res), dg, 1e-6, workspace=work)
         torch.cuda.synchronize()
-        assert int(work[:4].view(torch.int32).item()) == 0, "completion counter not reset"
+        assert rpl.rpl_matmul_reduce_rmsnorm_status(work) == 0
         outs.append((host_bf16(y), host_bf16(ro)))
     for y, ro in outs[1:]:
         assert np.array_equal(y, outs[0][0]) and np.array_equal(ro, outs[0][1])
+    # every call advances every workgroup's call count by one (the tag's source), whatever the grid
+    counts = work[256:256 + 4 * 1024].view(torch.int32)
+    assert bool((counts == 3).all())
     # residual_out may be the residual buffer itself
     r_in = dev_bf16(res)
     y2, ro2 = rpl.rpl_matmul_reduce_rmsnorm(dx, dw, r_in, dg, 1e-6, workspace=work, residual_out=r_in)
     assert ro2.data_ptr() == r_in.data_ptr()
     assert np.array_equal(host_bf16(r_in), outs[0][1]) and np.array_equal(host_bf16(y2), outs[0][0])
+
+
+def test_fused_one_workspace_across_shapes():
+    """Calls of different row counts, widths and shard counts share one workspace (sized for the
+    largest): slots a call does not write keep older tags, which no later call may take."""
+    import torch
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(16, 1024, 4)
+    for i, (m, n, k, tp) in enumerate([(16, 1024, 256, 4), (4, 1024, 256, 2), (16, 1024, 128, 4), (9, 512, 64, 3),
+                                       (16, 1024, 256, 4), (1, 8, 8, 1), (16, 1024, 64, 2)]):
+        say(f"[fused shared workspace] call {i}: m={m} n={n} k={k} tp={tp}")
+        xs, ws, res, gam = _inputs(m, m, n, k, tp, seed=40 + i)
+        y, ro = rpl.rpl_matmul_reduce_rmsnorm([dev_bf16(x) for x in xs], [dev_bf16(w) for w in ws], dev_bf16(res),
+                                              dev_bf16(gam), 1e-6, workspace=work)
+        wy, wro = _oracle_step(xs, ws, m, res, gam, 1e-6)
+        assert_bf16_close(host_bf16(ro), wro, f"call {i} residual_out")
+        assert_bf16_close(host_bf16(y), wy, f"call {i} y")
+    torch.cuda.synchronize()
+    assert rpl.rpl_matmul_reduce_rmsnorm_status(work) == 0
+
+
+def test_fused_wait_bound_reported():
+    """A wait bound set from the host to a single re-read (no spin needed to test it): a workgroup
+    that finds another's slot not yet written gives up, raises the status word and writes NaN to
+    its y columns (and, if it was waiting for a product, hands on a NaN sum of squares, so every
+    y that would depend on it is NaN as well); a y that is not NaN is right, the kernel exits
+    normally, and after the bound is lifted the same workspace gives the full result again."""
+    import torch
+    m, n, k, tp = 4, 3584, 1792, 2
+    xs, ws, res, gam = _inputs(m, m, n, k, tp, seed=8)
+    dx, dw, dr, dg = [dev_bf16(x) for x in xs], [dev_bf16(w) for w in ws], dev_bf16(res), dev_bf16(gam)
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(m, n, tp)
+    wy, wro = _oracle_step(xs, ws, m, res, gam, 1e-6)
+    rpl.rpl_matmul_reduce_rmsnorm_set_poll_bound(work, 1)
+    y, ro = rpl.rpl_matmul_reduce_rmsnorm(dx, dw, dr, dg, 1e-6, workspace=work)
+    torch.cuda.synchronize()
+    status = rpl.rpl_matmul_reduce_rmsnorm_status(work)
+    yh = host_bf16(y)
+    nan_cols = np.isnan(synth.bf16_decode(yh)).any(axis=0)
+    say(f"  bound of one re-read: status {status}, {int(nan_cols.sum())} of {n} columns NaN")
+    if status == 0:
+        assert not nan_cols.any()
+    else:
+        assert nan_cols.any()
+    assert_bf16_close(yh[:, ~nan_cols], wy[:, ~nan_cols], "y outside the given-up columns")
+    rpl.rpl_matmul_reduce_rmsnorm_set_poll_bound(work, 0)
+    work[8:12].zero_()
+    y, ro = rpl.rpl_matmul_reduce_rmsnorm(dx, dw, dr, dg, 1e-6, workspace=work)
+    torch.cuda.synchronize()
+    assert rpl.rpl_matmul_reduce_rmsnorm_status(work) == 0
+    assert_bf16_close(host_bf16(ro), wro, "residual_out after the bound is lifted")
+    assert_bf16_close(host_bf16(y), wy, "y after the bound is lifted")
 
 
 def test_fused_equals_unfused_library_path():

@@ -4,8 +4,9 @@ The decode-sized paths are timed by replaying HIP graphs, and a caller may captu
 Each case captures a sequence of calls once, then several times changes the inputs in place,
 runs the same calls eagerly, and replays the graph with eager work and synchronisation in
 between: every replay must reproduce the eager outputs bit for bit (the same kernels on the
-same bytes).  The single-launch decode path keeps a completion counter in its workspace that
-each launch resets itself, which repeated replays rely on.  The expected values here are the
+same bytes).  The single-launch decode path hands values between its workgroups through tagged
+slots in its workspace, the tag coming from a ticket every launch advances; repeated replays
+rely on that, and the workspace's status word must stay zero.  The expected values here are the
 library's own eager results: this checks capture and replay, parity with the oracle is checked
 elsewhere."""
 import pytest
@@ -86,7 +87,7 @@ def test_graph_single_launch_decode(rows):
     gam = torch.empty((n,), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
     ro = torch.empty((rows, n), dtype=torch.bfloat16, device="cuda")
-    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(rows, n)
+    work = rpl.rpl_matmul_reduce_rmsnorm_workspace(rows, n, tp)
 
     def refill(rep):
         for t in xs:
@@ -101,8 +102,7 @@ def test_graph_single_launch_decode(rows):
 
     refill(-1)
     _check_replays(f"single-launch decode, {rows} rows", run, [y, ro], refill)
-    counter = work[:4].view(torch.int32)
-    assert int(counter.item()) == 0, "the completion counter must be back at zero after every launch"
+    assert rpl.rpl_matmul_reduce_rmsnorm_status(work) == 0, "no wait may have given up"
 
 
 def test_graph_w8a8_dynamic_and_prefill_tiles():

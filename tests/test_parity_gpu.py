@@ -5,8 +5,9 @@ Same seeded inputs on both sides.  bf16 outputs must satisfy
 be bit-exact; w8a8 int32 accumulators must be bit-exact and their dequantised
 bf16 outputs within 1e-3 relative.  Small shapes are compared in full (several
 tiles plus ragged tails); the full-size workloads run in the same launch
-configuration as bench.py and are compared on sampled rows that the oracle
-computes one by one.
+configuration as bench.py and are compared element by element too (the oracle's
+products of a workload are computed once per session and shared by the tests
+that need them).
 """
 import numpy as np
 import pytest
@@ -31,13 +32,6 @@ def shards(x_full, w_full, tp):
     ks = x_full.shape[1] // tp
     return [(np.ascontiguousarray(x_full[:, s * ks:(s + 1) * ks]),
              np.ascontiguousarray(w_full[:, s * ks:(s + 1) * ks])) for s in range(tp)]
-
-
-def sample_rows(m_pad, extra=8, seed=0):
-    fixed = {0, 1, 15, 16, 17, 255, 256, 257, m_pad // 2 - 1, m_pad // 2, m_pad - 2, m_pad - 1}
-    rng = np.random.default_rng(seed)
-    rows = sorted({r for r in fixed if 0 <= r < m_pad} | set(rng.integers(0, m_pad, extra).tolist()))
-    return np.array(rows, dtype=np.int64)
 
 
 # (m, n, k_full, tp): ragged m, n, K; pad rows; both kernels; full and partial tiles
@@ -99,18 +93,41 @@ def test_partial_exact_cases(m, n, k):
     assert np.array_equal(got, want)
 
 
+# oracle products of the full-size workloads, computed once per session
+_ORACLE = {}
+
+
+def oracle_rank_partial(wl):
+    """The oracle's rank-0 partial of a workload, all M_pad rows."""
+    key = ("rank", wl.name)
+    if key not in _ORACLE:
+        say(f"  oracle: rank partial of {wl.name} ({wl.m} x {wl.n} x {wl.k_shard})")
+        _ORACLE[key] = oracle.partial_rows(synth.x_shard(wl, 0), synth.w_shard(wl, 0), wl.m, tp=wl.tp)
+    return _ORACLE[key]
+
+
+def oracle_peer_chunk(wl, s):
+    """The oracle's chunk-0 partial of peer shard s (its first m_chunk rows)."""
+    key = ("peer", wl.name, s)
+    if key not in _ORACLE:
+        say(f"  oracle: peer {s} chunk partial of {wl.name}")
+        _ORACLE[key] = oracle.partial_rows(synth.x_shard(wl, s, rows=wl.m_chunk), synth.w_shard(wl, s),
+                                           wl.m_chunk)
+    return _ORACLE[key]
+
+
 @pytest.mark.parametrize("wid", [2, 3, 4])
-def test_partial_full_size_sampled(wid):
+def test_partial_full_size(wid):
+    """Every output element of the rank partial at the workload's full size."""
     wl = synth.WORKLOADS[wid]
     say(f"[partial full] {wl.name}")
     x, w = synth.x_shard(wl, 0), synth.w_shard(wl, 0)
     out = rpl.rpl_partial(dev_bf16(x), dev_bf16(w), wl.tp)
     got = host_bf16(out)
     assert got.shape == (wl.m_pad, wl.n)
-    rows = sample_rows(wl.m_pad)
-    want = oracle.partial_rows(x, w, wl.m, rows=rows, tp=wl.tp)
-    err = assert_bf16_close(got[rows], want, f"{wl.name} sampled rows")
-    say(f"  max abs err {err:.3g} over {rows.size} rows")
+    want = oracle_rank_partial(wl)
+    err = assert_bf16_close(got, want, f"{wl.name} all elements")
+    say(f"  max abs err {err:.3g} over {got.size} elements")
     assert np.all(np.isfinite(f64(got)))
 
 
@@ -197,13 +214,18 @@ def test_received_chunk_end_to_end(wid):
     own = rpl.rpl_partial(dev_bf16(xs[0]), dev_bf16(ws[0]), wl.tp)
     chunks = [own[:mc]] + [rpl.rpl_partial(dev_bf16(xs[s]), dev_bf16(ws[s]), 1) for s in range(1, wl.tp)]
     y, ro = rpl.rpl_reduce_chunk_rmsnorm(chunks, dev_bf16(res), dev_bf16(gam), wl.eps)
-    rows = np.arange(mc) if mc <= 64 else sample_rows(mc, extra=6)
-    o_parts = [oracle.partial_rows(xs[s], ws[s], wl.m if s == 0 else mc, rows=rows, tp=wl.tp if s == 0 else 1)
-               for s in range(wl.tp)]
-    wy, wro = oracle.reduce_chunk_rmsnorm(o_parts, res[rows], gam, wl.eps)
-    e1 = assert_bf16_close(host_bf16(ro)[rows], wro, f"{wl.name} residual_out")
-    e2 = assert_bf16_close(host_bf16(y)[rows], wy, f"{wl.name} y")
-    say(f"  max abs err residual_out {e1:.3g} y {e2:.3g} over {rows.size} rows")
+    if mc <= 64:
+        o_parts = [oracle.partial_rows(xs[s], ws[s], wl.m if s == 0 else mc, rows=np.arange(mc),
+                                       tp=wl.tp if s == 0 else 1) for s in range(wl.tp)]
+    else:  # every row of the chunk, from the session's oracle products
+        o_parts = [np.ascontiguousarray(oracle_rank_partial(wl)[:mc])]
+        o_parts += [oracle_peer_chunk(wl, s) for s in range(1, wl.tp)]
+        for s in range(1, wl.tp):
+            assert_bf16_close(host_bf16(chunks[s]), o_parts[s], f"{wl.name} peer {s} chunk partial")
+    wy, wro = oracle.reduce_chunk_rmsnorm(o_parts, res, gam, wl.eps)
+    e1 = assert_bf16_close(host_bf16(ro), wro, f"{wl.name} residual_out")
+    e2 = assert_bf16_close(host_bf16(y), wy, f"{wl.name} y")
+    say(f"  max abs err residual_out {e1:.3g} y {e2:.3g} over all {mc} rows")
 
 
 def test_partial_row_stride_at_the_limit():
@@ -275,15 +297,17 @@ def test_w8a8_near_int32_limit():
     assert_rel(host_bf16(out), wout, "dequantised output")
 
 
-def test_w8a8_full_size_sampled():
+def test_w8a8_full_size():
+    """Every int32 accumulator and every dequantised output of the w8a8 workload."""
     wl = synth.WORKLOADS[5]
     say(f"[w8a8 full] {wl.name}")
     xq, sx, wq, sw = synth.w8a8_inputs(wl)
     out, acc = rpl.rpl_w8a8_partial(dev(xq), dev(sx), dev(wq), dev(sw), wl.tp, want_acc=True)
-    rows = sample_rows(wl.m_pad)
-    wout, wacc = oracle.w8a8_rows(xq, sx, wq, sw, wl.m, rows=rows, tp=wl.tp)
-    assert np.array_equal(acc.cpu().numpy()[rows], wacc)
-    assert_rel(host_bf16(out)[rows], wout, "dequantised output")
+    say(f"  oracle: w8a8 rank partial of {wl.name}")
+    wout, wacc = oracle.w8a8_rows(xq, sx, wq, sw, wl.m, tp=wl.tp)
+    assert np.array_equal(acc.cpu().numpy(), wacc), "int32 accumulators must be bit-exact"
+    assert_rel(host_bf16(out), wout, "dequantised output")
+    assert np.array_equal(host_bf16(out), wout), "dequantised output bit-exact under the pinned fp32 order"
     # the timed configuration (no accumulator store) gives the same output bits
     out2 = rpl.rpl_w8a8_partial(dev(xq), dev(sx), dev(wq), dev(sw), wl.tp)
     assert np.array_equal(host_bf16(out2), host_bf16(out))

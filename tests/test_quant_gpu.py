@@ -89,7 +89,7 @@ def test_quant_workload_activation(wid):
     _compare(xq, sx, wq, ws, wl.name)
 
 
-def _dynamic_step(wl, rows_for_oracle):
+def _dynamic_step(wl, rows_for_oracle, full_own=False):
     """bf16 X shards -> quantiser -> int8 partials -> reduce + RMSNorm on chunk 0."""
     mc = wl.m_chunk
     xs = [synth.x_shard(wl, 0)] + [synth.x_shard(wl, s, rows=mc) for s in range(1, wl.tp)]
@@ -105,6 +105,12 @@ def _dynamic_step(wl, rows_for_oracle):
     rows = rows_for_oracle
     o_parts = []
     for s in range(wl.tp):
+        if s == 0 and full_own:  # all the rank's rows, chunk 0 among them
+            oq, osc = oracle.quant_per_token(xs[0])
+            o_all, _ = oracle.w8a8_rows(oq, osc, wts[0][0], wts[0][1], wl.m, tp=wl.tp)
+            assert np.array_equal(host_bf16(own), o_all), "own int8 partial differs"
+            o_parts.append(np.ascontiguousarray(o_all[rows]))
+            continue
         oq, osc = oracle.quant_per_token(xs[s], rows=int(rows.max()) + 1 if rows.size else 0)
         o_out, _ = oracle.w8a8_rows(oq, osc, wts[s][0], wts[s][1], wl.m if s == 0 else mc, rows=rows,
                                     tp=wl.tp if s == 0 else 1)
@@ -125,10 +131,9 @@ def test_w8a8_dynamic_small_end_to_end():
     _dynamic_step(wl, np.arange(wl.m_chunk, dtype=np.int64))
 
 
-def test_w8a8_dynamic_full_size_sampled():
+def test_w8a8_dynamic_full_size():
+    """The w8a8_dynamic step at full size: every code, every int8 partial output of the rank
+    (all 4096 rows) and of the peer's chunk, and every element of the received chunk."""
     wl = synth.WORKLOADS[5]
     say(f"[w8a8 dynamic full] {wl.name}")
-    rng = np.random.default_rng(11)
-    rows = np.array(sorted({0, 1, 255, 256, wl.m_chunk - 1} | set(rng.integers(0, wl.m_chunk, 6).tolist())),
-                    dtype=np.int64)
-    _dynamic_step(wl, rows)
+    _dynamic_step(wl, np.arange(wl.m_chunk, dtype=np.int64), full_own=True)
