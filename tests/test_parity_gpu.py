@@ -15,7 +15,8 @@ import pytest
 import oracle
 import row_matmul_reduce_amd as rpl
 from row_matmul_reduce_amd import synth
-from gpu_util import (assert_bf16_close, assert_rel, dev, dev_bf16, f64, host_bf16, say)
+from gpu_util import (assert_bf16_close, assert_rel, assert_sum_close, dev, dev_bf16, f64, host_bf16, say,
+                      y_scale)
 
 pytestmark = pytest.mark.gpu
 
@@ -204,7 +205,11 @@ def test_reduce_zero_row_and_unit_rms():
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_received_chunk_end_to_end(wid):
-    """Rank 0's step: own partial + every peer's chunk-0 partial -> reduce + RMSNorm."""
+    """Rank 0's step: own partial + every peer's chunk-0 partial -> reduce + RMSNorm, every
+    element.  Stage by stage against the oracle: each partial (bf16 rule), then the reduce and
+    RMSNorm on the very partials the GPU produced (bf16 rule); and end to end against the
+    oracle's own partials, where the bound adds one bf16 ulp per summed partial (two sides'
+    partials may each differ by one ulp, and the sum keeps those differences)."""
     wl = synth.WORKLOADS[wid]
     say(f"[end-to-end] {wl.name}")
     mc = wl.m_chunk
@@ -220,12 +225,20 @@ def test_received_chunk_end_to_end(wid):
     else:  # every row of the chunk, from the session's oracle products
         o_parts = [np.ascontiguousarray(oracle_rank_partial(wl)[:mc])]
         o_parts += [oracle_peer_chunk(wl, s) for s in range(1, wl.tp)]
-        for s in range(1, wl.tp):
-            assert_bf16_close(host_bf16(chunks[s]), o_parts[s], f"{wl.name} peer {s} chunk partial")
+    g_parts = [host_bf16(c) for c in chunks]
+    for s in range(wl.tp):
+        assert_bf16_close(g_parts[s], o_parts[s], f"{wl.name} shard {s} chunk partial")
+    gy, gro = host_bf16(y), host_bf16(ro)
+    # the reduce + RMSNorm on the GPU's own partials
+    wy_g, wro_g = oracle.reduce_chunk_rmsnorm(g_parts, res, gam, wl.eps)
+    e1 = assert_bf16_close(gro, wro_g, f"{wl.name} residual_out on the GPU partials")
+    e2 = assert_bf16_close(gy, wy_g, f"{wl.name} y on the GPU partials")
+    # end to end against the oracle's partials
     wy, wro = oracle.reduce_chunk_rmsnorm(o_parts, res, gam, wl.eps)
-    e1 = assert_bf16_close(host_bf16(ro), wro, f"{wl.name} residual_out")
-    e2 = assert_bf16_close(host_bf16(y), wy, f"{wl.name} y")
-    say(f"  max abs err residual_out {e1:.3g} y {e2:.3g} over all {mc} rows")
+    n1 = assert_sum_close(gro, wro, o_parts, f"{wl.name} residual_out end to end")
+    n2 = assert_sum_close(gy, wy, o_parts, f"{wl.name} y end to end", scale=y_scale(wro, gam, wl.eps))
+    say(f"  max abs err on the GPU partials: residual_out {e1:.3g} y {e2:.3g}; end to end {n1} + {n2} of "
+        f"{gro.size} elements need the per-partial ulp term, all rows")
 
 
 def test_partial_row_stride_at_the_limit():
