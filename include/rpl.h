@@ -348,6 +348,35 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
                                      void *stream);
 
 /*
+ * rpl_matmul_reduce_rmsnorm_noalloc -- rpl_matmul_reduce_rmsnorm for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, results and checks
+ * without the workspace: the hand-offs between the launch's workgroups use a
+ * device array inside the library (4 MiB, each GPU the library runs on holds
+ * its own copy until the process ends; it starts zero-filled and every call
+ * leaves it ready for the next, so nothing needs clearing).  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine); the
+ * caller passes the inputs and outputs.  All calls of this function on one GPU
+ * share that GPU's array: calls that overlap in time on one GPU (on different
+ * streams) race, so the caller must order them (one stream is enough).  Calls
+ * of rpl_matmul_reduce_rmsnorm with their own workspaces do not touch it.
+ *
+ * RPL_ERR_UNSUPPORTED also when the hand-off memory the shape needs,
+ *                     rpl_matmul_reduce_rmsnorm_workspace_size(m, n, tp),
+ *                     exceeds 4 MiB (e.g. m = 8, n = 3584, tp = 2 needs
+ *                     233,728 bytes; with m = 64, n * tp may be at most 16,367)
+ * RPL_ERR_LAUNCH      also when the array's device address cannot be looked up
+ *                     on the current device
+ */
+rpl_status rpl_matmul_reduce_rmsnorm_noalloc(const rpl_bf16 *const *x_shards, int64_t ldx,
+                                             const rpl_bf16 *const *w_shards, int64_t ldw,
+                                             int32_t tp, int64_t m, int64_t m_valid,
+                                             int64_t n, int64_t k,
+                                             const rpl_bf16 *residual, const rpl_bf16 *gamma,
+                                             float eps, rpl_bf16 *y, rpl_bf16 *residual_out,
+                                             void *stream);
+
+/*
  * rpl_shard_rows / rpl_gather_rows -- the token-row movement around the
  * exchange in the FlashComm1 layout.
  *
@@ -385,7 +414,7 @@ rpl_status rpl_gather_rows(const rpl_bf16 *const *chunks, int32_t tp, int64_t m_
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 2.0. */
+/* Library ABI version: (major << 16) | minor.  Currently 2.1. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.rpl_matmul_reduce_rmsnorm.restype = ctypes.c_int
         L.rpl_matmul_reduce_rmsnorm.argtypes = [_p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _p,
                                                 ctypes.c_float, _p, _p, _p, _i64, _p]
+        L.rpl_matmul_reduce_rmsnorm_noalloc.restype = ctypes.c_int
+        L.rpl_matmul_reduce_rmsnorm_noalloc.argtypes = [_p, _i64, _p, _i64, _i32, _i64, _i64, _i64, _i64, _p, _p,
+                                                         ctypes.c_float, _p, _p, _p]
         L.rpl_sum_partials.restype = ctypes.c_int
         L.rpl_sum_partials.argtypes = [_p, _i32, _i64, _i64, _i64, _p, _p]
         L.rpl_reduce_slice_sumsq.restype = ctypes.c_int
@@ -428,9 +431,39 @@ def rpl_read_ceiling(t, grid: int, sink, stream=None):
     _check("rpl_read_ceiling", st)
 
 
+def rpl_matmul_reduce_rmsnorm_noalloc(x_shards, w_shards, residual, gamma, eps: float, y, residual_out,
+                                      stream=None):
+    """rpl_matmul_reduce_rmsnorm without a workspace, for callers that cannot allocate: the
+    library's own device array carries the hand-offs (calls on one GPU must not overlap in
+    time).  y and residual_out must be given; nothing is allocated.  Returns (y, residual_out)."""
+    torch = _torch()
+    tp = len(w_shards)
+    if tp < 1 or len(x_shards) != tp:
+        raise ValueError("need as many activation shards as weight shards (at least one)")
+    _dev(residual, "residual", torch.bfloat16, 2)
+    _dev(gamma, "gamma", torch.bfloat16, 1)
+    _dev(y, "y", torch.bfloat16, 2)
+    _dev(residual_out, "residual_out", torch.bfloat16, 2)
+    m, n = residual.shape
+    k = w_shards[0].shape[1]
+    m_valid = x_shards[0].shape[0]
+    if any(t.shape != (n, k) for t in w_shards) or any(t.shape != (m_valid, k) for t in x_shards):
+        raise ValueError("shard shapes disagree")
+    ldx, ldw = _ld(x_shards[0]), _ld(w_shards[0])
+    if any(_ld(t) != ldx for t in x_shards) or any(_ld(t) != ldw for t in w_shards):
+        raise ValueError("all shards must share one row stride")
+    xs = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in x_shards])
+    ws = (ctypes.c_void_p * tp)(*[t.data_ptr() for t in w_shards])
+    st = lib().rpl_matmul_reduce_rmsnorm_noalloc(ctypes.cast(xs, _p), ldx, ctypes.cast(ws, _p), ldw, tp, m, m_valid,
+                                                 n, k, residual.data_ptr(), gamma.data_ptr(), float(eps),
+                                                 y.data_ptr(), residual_out.data_ptr(), _stream(residual, stream))
+    _check("rpl_matmul_reduce_rmsnorm_noalloc", st)
+    return y, residual_out
+
+
 __all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_quant_per_token",
            "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace", "rpl_matmul_reduce_rmsnorm_status",
-           "rpl_matmul_reduce_rmsnorm_set_poll_bound", "rpl_sum_partials",
+           "rpl_matmul_reduce_rmsnorm_set_poll_bound", "rpl_matmul_reduce_rmsnorm_noalloc", "rpl_sum_partials",
            "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
            "rpl_status_string", "rpl_version", "rpl_read_ceiling",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

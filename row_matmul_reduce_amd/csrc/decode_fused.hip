@@ -47,6 +47,7 @@
 // guarantee but measured about 20 us more per launch here.)
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "rpl_device.h"
 #include "rpl_launch.h"
@@ -305,6 +306,35 @@ decode_fused_kernel(FusedDecodeArgs a) {
 // the poll bound (0 = default), [256, 256 + 4 * FD_MAX_GRID) the workgroups' call counts; from
 // FD_WS_HEADER the product slots [m][tp][n / 2], 8 bytes each.
 int64_t fused_decode_workspace_bytes(int64_t m, int64_t n, int64_t tp) { return FD_WS_HEADER + 4 * m * tp * n; }
+
+// Hand-off memory of rpl_matmul_reduce_rmsnorm_noalloc, for callers that cannot allocate: the
+// same layout as a caller's workspace, in a file-scope device array that each GPU holds until the
+// process ends.  Static storage starts zero-filled, which is all the hand-off protocol needs:
+// calls leave it ready for the next one, so nothing is cleared between calls.
+static __device__ __align__(256) uint8_t scratch[FD_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current device.  In host code the array's name is a
+// host-side stand-in, not a device address: the address is looked up once per device (with that
+// device current) and kept; kernels only ever receive the looked-up pointer.
+hipError_t fused_decode_scratch(void **ptr) {
+    constexpr int MAX_DEV = 64;
+    static std::mutex mu;
+    static void *addr[MAX_DEV];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // Workgroups of one kernel variant the current device holds at once, at most FD_MAX_GRID
 // (looked up once per device and variant).

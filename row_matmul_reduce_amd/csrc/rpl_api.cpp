@@ -280,14 +280,21 @@ int64_t rpl_matmul_reduce_rmsnorm_workspace_size(int64_t m, int64_t n, int32_t t
     return rpl::fused_decode_workspace_bytes(m, n, tp);
 }
 
-rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx, const rpl_bf16 *const *w_shards,
-                                     int64_t ldw, int32_t tp, int64_t m, int64_t m_valid, int64_t n, int64_t k,
-                                     const rpl_bf16 *residual, const rpl_bf16 *gamma, float eps, rpl_bf16 *y,
-                                     rpl_bf16 *residual_out, void *workspace, int64_t workspace_bytes,
-                                     void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of the single-launch decode path shared by its two entry points (workspace != NULL:
+// the caller's workspace of workspace_bytes; NULL: the library's static hand-off memory, which
+// needs fused_decode_workspace_bytes <= FD_SCRATCH_BYTES).  Fills the kernel arguments except
+// the hand-off pointers.
+rpl_status fused_check(const rpl_bf16 *const *x_shards, int64_t ldx, const rpl_bf16 *const *w_shards, int64_t ldw,
+                       int32_t tp, int64_t m, int64_t m_valid, int64_t n, int64_t k, const rpl_bf16 *residual,
+                       const rpl_bf16 *gamma, float eps, rpl_bf16 *y, rpl_bf16 *residual_out, const void *workspace,
+                       int64_t workspace_bytes, bool own_scratch, rpl::FusedDecodeArgs &a) {
     if (!x_shards || !w_shards || !gamma) return RPL_ERR_NULL;
     if (m != 0) {
-        if (!residual || !y || !residual_out || !workspace) return RPL_ERR_NULL;
+        if (!residual || !y || !residual_out || (!own_scratch && !workspace)) return RPL_ERR_NULL;
         if (tp >= 1 && tp <= RPL_MAX_TP)
             for (int s = 0; s < tp; ++s)
                 if (!w_shards[s] || (m_valid > 0 && !x_shards[s])) return RPL_ERR_NULL;
@@ -299,8 +306,8 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
     const int64_t mat = span(m, n, n, 2), gb = span(1, n, n, 2);
     const int64_t xb = span(m_valid, k, ldx, 2), wb = span(n, k, ldw, 2);
     const int64_t need = (m <= 64 && n <= rpl::FD_MAX_N && np) ? rpl::fused_decode_workspace_bytes(m, n, tp) : 0;
-    if (m != 0 && workspace_bytes < need) return RPL_ERR_INVALID;
-    const int64_t wsb = workspace_bytes < 0 ? 0 : workspace_bytes;
+    if (!own_scratch && m != 0 && workspace_bytes < need) return RPL_ERR_INVALID;
+    const int64_t wsb = own_scratch || workspace_bytes < 0 ? 0 : workspace_bytes;
     // outputs and workspace against the inputs and each other
     const void *outs[3] = {y, residual_out, workspace};
     const int64_t osz[3] = {mat, mat, wsb};
@@ -316,14 +323,13 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
     }
     if (tp > RPL_MAX_TP || m > 64 || n > rpl::FD_MAX_N || n % 8 || k % 8 || ldx % 8 || ldw % 8)
         return RPL_ERR_UNSUPPORTED;
+    if (own_scratch && need > rpl::FD_SCRATCH_BYTES) return RPL_ERR_UNSUPPORTED;
     if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(y, 16) || !aligned(residual_out, 16) ||
-        !aligned(workspace, 256))
+        (!own_scratch && !aligned(workspace, 256)))
         return RPL_ERR_UNSUPPORTED;
     for (int s = 0; s < tp; ++s)
         if (!aligned(w_shards[s], 16) || !aligned(x_shards[s], 16)) return RPL_ERR_UNSUPPORTED;
     if (k > kMaxDim) return RPL_ERR_UNSUPPORTED;
-    if (m == 0) return RPL_OK;
-    rpl::FusedDecodeArgs a{};
     for (int s = 0; s < tp; ++s) {
         a.x[s] = x_shards[s];
         a.w[s] = w_shards[s];
@@ -340,11 +346,46 @@ rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ld
     a.eps = eps;
     a.y = y;
     a.residual_out = residual_out;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    return RPL_OK;
+}
+
+void fused_handoff(rpl::FusedDecodeArgs &a, void *mem) {
+    uint8_t *ws = static_cast<uint8_t *>(mem);
     a.calls = reinterpret_cast<unsigned *>(ws + 256);
     a.status = reinterpret_cast<unsigned *>(ws + 8);
     a.poll_limit = reinterpret_cast<const unsigned *>(ws + 12);
     a.p_slots = reinterpret_cast<unsigned long long *>(ws + rpl::FD_WS_HEADER);
+}
+
+}  // namespace
+
+extern "C" {
+
+rpl_status rpl_matmul_reduce_rmsnorm(const rpl_bf16 *const *x_shards, int64_t ldx, const rpl_bf16 *const *w_shards,
+                                     int64_t ldw, int32_t tp, int64_t m, int64_t m_valid, int64_t n, int64_t k,
+                                     const rpl_bf16 *residual, const rpl_bf16 *gamma, float eps, rpl_bf16 *y,
+                                     rpl_bf16 *residual_out, void *workspace, int64_t workspace_bytes,
+                                     void *stream) {
+    rpl::FusedDecodeArgs a{};
+    const rpl_status st = fused_check(x_shards, ldx, w_shards, ldw, tp, m, m_valid, n, k, residual, gamma, eps, y,
+                                      residual_out, workspace, workspace_bytes, false, a);
+    if (st != RPL_OK || m == 0) return st;
+    fused_handoff(a, workspace);
+    return launch_status(rpl::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
+}
+
+rpl_status rpl_matmul_reduce_rmsnorm_noalloc(const rpl_bf16 *const *x_shards, int64_t ldx,
+                                             const rpl_bf16 *const *w_shards, int64_t ldw, int32_t tp, int64_t m,
+                                             int64_t m_valid, int64_t n, int64_t k, const rpl_bf16 *residual,
+                                             const rpl_bf16 *gamma, float eps, rpl_bf16 *y, rpl_bf16 *residual_out,
+                                             void *stream) {
+    rpl::FusedDecodeArgs a{};
+    const rpl_status st = fused_check(x_shards, ldx, w_shards, ldw, tp, m, m_valid, n, k, residual, gamma, eps, y,
+                                      residual_out, nullptr, 0, true, a);
+    if (st != RPL_OK || m == 0) return st;
+    void *mem = nullptr;
+    if (rpl::fused_decode_scratch(&mem) != hipSuccess) return RPL_ERR_LAUNCH;
+    fused_handoff(a, mem);
     return launch_status(rpl::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -359,6 +400,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (2 << 16) | 0; }
+int32_t rpl_version(void) { return (2 << 16) | 1; }
 
 }  // extern "C"

@@ -48,6 +48,10 @@ struct FusedDecodeArgs {
     unsigned long long *p_slots;      // [m][tp][n / 2]
 };
 int64_t fused_decode_workspace_bytes(int64_t m, int64_t n, int64_t tp);
+// The no-allocation form's hand-off memory: a static device array of this size, and its
+// device address on the current device.
+constexpr int64_t FD_SCRATCH_BYTES = int64_t(4) << 20;
+hipError_t fused_decode_scratch(void **ptr);
 hipError_t launch_decode_fused(const FusedDecodeArgs &a, hipStream_t st);
 
 hipError_t launch_sum_partials(const PartialPtrs &p, int tp, int m, int n, int64_t ldp, uint16_t *out,

@@ -56,7 +56,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (2 << 16) | 0
+    assert rpl.rpl_version() == (2 << 16) | 1
 
 
 class Buf:
@@ -428,3 +428,39 @@ def test_read_ceiling_validation():
     assert call(B.ptr + 8, 4080, 256, S.ptr) == UNSUP
     assert call(B.ptr, 4096, 256, S.ptr + 2) == UNSUP
     assert B.untouched() and S.untouched()
+
+
+def test_fused_noalloc_validation():
+    """The no-allocation form checks like the workspace form (no workspace arguments) and refuses
+    shapes whose hand-off memory exceeds its 4 MiB array, all on the host before any HIP call."""
+    import ctypes
+    L = rpl.lib()
+    tp, m, n, k = 2, 4, 64, 32
+    X0, X1, W0, W1 = Buf(m * k * 2), Buf(m * k * 2), Buf(n * k * 2), Buf(n * k * 2)
+    R, G, Y, RO = Buf(m * n * 2), Buf(n * 2), Buf(m * n * 2), Buf(m * n * 2)
+
+    def call(xs=None, ws=None, **kw):
+        a = dict(ldx=k, ldw=k, tp=tp, m=m, mv=m, n=n, k=k, res=R.ptr, gam=G.ptr, eps=1e-6, y=Y.ptr, ro=RO.ptr)
+        a.update(kw)
+        xs = xs if xs is not None else [X0.ptr, X1.ptr]
+        ws = ws if ws is not None else [W0.ptr, W1.ptr]
+        xa = (ctypes.c_void_p * len(xs))(*xs)
+        wa = (ctypes.c_void_p * len(ws))(*ws)
+        return L.rpl_matmul_reduce_rmsnorm_noalloc(ctypes.cast(xa, ctypes.c_void_p), a["ldx"],
+                                                   ctypes.cast(wa, ctypes.c_void_p), a["ldw"], a["tp"], a["m"],
+                                                   a["mv"], a["n"], a["k"], a["res"], a["gam"], a["eps"], a["y"],
+                                                   a["ro"], None)
+
+    cases = [
+        (dict(xs=[X0.ptr, None]), NULL), (dict(res=None), NULL), (dict(gam=None), NULL), (dict(ro=None), NULL),
+        (dict(m=-1), INVALID), (dict(mv=5), INVALID), (dict(n=0), INVALID), (dict(ldw=24), INVALID),
+        (dict(eps=-1.0), INVALID), (dict(y=R.ptr), INVALID), (dict(ro=Y.ptr), INVALID),
+        (dict(n=60), UNSUP), (dict(m=65, mv=4), UNSUP), (dict(y=Y.ptr + 8), UNSUP),
+        # hand-off memory of 4,352 + 4 * 64 * 2 * 8192 bytes > 4 MiB (fake device pointers: refused first)
+        (dict(m=64, mv=0, n=8192, res=1 << 40, y=1 << 41, ro=1 << 42, gam=1 << 43), UNSUP),
+    ]
+    for kw, want in cases:
+        assert call(**kw) == want, kw
+    for b in (X0, X1, W0, W1, R, G, Y, RO):
+        assert b.untouched()
+    assert call(m=0, mv=0, res=None, y=None, ro=None) == OK
