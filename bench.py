@@ -57,10 +57,12 @@ KERNEL_SOURCES = {
     "decode_fused": ["decode_fused.hip", "rpl_device.h"],
     "reduce_variants": ["reduce_variants.hip", "rpl_device.h"],
     "token_rows": ["token_rows.hip", "rpl_device.h"],
+    "read_ceiling": ["read_ceiling.hip", "rpl_device.h"],
 }
 # kernels that live in a shared source file
 KERNEL_KEY = {"sum_partials": "reduce_variants", "slice_sumsq": "reduce_variants", "slice_apply": "reduce_variants",
-              "token_rows_gather": "token_rows", "token_rows_shard": "token_rows"}
+              "token_rows_gather": "token_rows", "token_rows_shard": "token_rows",
+              "decode_fused_chunk": "decode_fused", "decode_fused_allrows": "decode_fused"}
 WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "long_prefill": 4, "w8a8": 5, "w8a8_dynamic": 5}
 
 
@@ -680,6 +682,268 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+# ------------------------------------------------------------------ rocprofv3 summaries
+# The profiles/ summaries come from these runs of this file under rocprofv3 (each in its own run;
+# <dir> is where rocprofv3 writes), then `python bench.py --rocprof-summary <dir>`.
+PROFILE_RUNS = {
+    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace -o bench -- "
+             "python3 /root/repo/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/fetch -o run -- "
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/write -o run -- "
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "cal_fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/cal_fetch -o run -- "
+                 "python3 /root/repo/bench.py --copy-calibration",
+    "cal_write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/cal_write -o run -- "
+                 "python3 /root/repo/bench.py --copy-calibration",
+    "mfma": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT -f csv "
+            "-d <dir>/mfma -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+}
+# The default run's phases, in order, each opened by the first dispatch whose name matches (after the
+# previous phase opened): the main bf16 prefill step, the two w8a8 steps, the decode step, the
+# decode plain-read ceiling, the long-prefill step, the single-launch decode path (with its
+# unfused composition), then the reduce variants and the token rows.
+PHASES = [("prefill", None), ("w8a8", "gemm_w8a8_wide_kernel"), ("decode", "gemm_bf16_decode_kernel"),
+          ("ceiling", "read_ceiling_kernel"), ("long", "gemm_bf16_wide_kernel"), ("fused", "decode_fused_kernel"),
+          ("rest", "sum_partials_kernel")]
+# (profile key, workload, full kernel-name prefix after "rpl::", phase, grid: None = most dispatches,
+#  "min" / "max" = smallest / largest grid, "all" = every grid)
+PROFILES = [
+    ("partial_bf16", "prefill_down_proj_7b", "gemm_bf16_wide_kernel<224, 3, false>", "prefill", None),
+    ("reduce_rmsnorm", "prefill_down_proj_7b", "reduce_rmsnorm_kernel<", "prefill", None),
+    ("partial_w8a8", "w8a8_prefill_down_proj_7b", "gemm_w8a8_wide_kernel<224, 3, false>", "w8a8", "max"),
+    ("quant_per_token", "w8a8_prefill_down_proj_7b", "quant_rows_kernel<", "w8a8", "max"),
+    ("partial_bf16", "decode_o_proj_7b", "gemm_bf16_decode_kernel<2>", "decode", None),
+    ("reduce_rmsnorm", "decode_o_proj_7b", "reduce_rmsnorm_kernel<", "decode", None),
+    ("read_ceiling", "decode_o_proj_7b", "read_ceiling_kernel", "ceiling", "all"),
+    ("partial_bf16", "long_prefill_tp8_share", "gemm_bf16_wide_kernel<224, 3, false>", "long", None),
+    ("reduce_rmsnorm", "long_prefill_tp8_share", "reduce_rmsnorm_kernel<", "long", None),
+    ("decode_fused_chunk", "decode_o_proj_7b", "decode_fused_kernel<1, 4>", "fused", None),
+    ("decode_fused_allrows", "decode_o_proj_7b", "decode_fused_kernel<1, 2>", "fused", None),
+    ("sum_partials", "prefill_down_proj_7b", "sum_partials_kernel", "rest", None),
+    ("slice_sumsq", "long_prefill_tp8_share", "slice_sumsq_kernel", "rest", None),
+    ("slice_apply", "long_prefill_tp8_share", "slice_apply_kernel", "rest", None),
+    ("token_rows_gather", "long_prefill_tp8_share", "token_rows_kernel", "rest", "max"),
+    ("token_rows_shard", "long_prefill_tp8_share", "token_rows_kernel", "rest", "min"),
+]
+PROFILE_NOTES = {
+    "decode_fused_chunk": "single-launch decode path on rank 0's 4-row token chunk, both shards' products",
+    "decode_fused_allrows": "single-launch decode path on all 8 rows (all-reduce form), both shards' products",
+    "read_ceiling": "plain streaming read of one rotated 12.85 MB weight copy per launch, at each grid the bench tries",
+    "token_rows_gather": "the 8 ranks' 2048-row blocks gathered back to all 16384 rows",
+    "token_rows_shard": "rank 0's 2048-row block of the 16384 rows",
+    "sum_partials": "all-reduce form: both ranks' partials summed over all 4096 rows",
+    "slice_sumsq": "hidden-split step 1: one rank's 640-column slice of the 2048-row chunk, 8 partials",
+    "slice_apply": "hidden-split step 2: the slice normalised with the 8 ranks' sums of squares",
+}
+
+
+def _profile_alg_bytes(key, w):
+    if key.startswith("partial"):
+        return w.partial_bytes()
+    if key == "reduce_rmsnorm":
+        return w.reduce_bytes()
+    if key == "quant_per_token":
+        return w.quant_bytes()
+    if key.startswith("decode_fused"):
+        rows = w.m_chunk if key.endswith("chunk") else w.m
+        return w.tp * w.n * w.k_shard * 2 + w.tp * rows * w.k_shard * 2 + 3 * rows * w.n * 2 + w.n * 2
+    if key == "read_ceiling":
+        return w.n * w.k_shard * 2
+    return {"sum_partials": 88080384, "slice_sumsq": 31465472, "slice_apply": 7931136,
+            "token_rows_gather": 335544320, "token_rows_shard": 41943040}[key]
+
+
+def _csv_rows(d, pattern):
+    import csv
+    import glob
+    fs = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+    if not fs:
+        return None
+    with open(fs[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _grid(r):
+    if r.get("Grid_Size") not in (None, ""):
+        return int(r["Grid_Size"])
+    g = 1
+    for a in ("X", "Y", "Z"):
+        v = r.get(f"Grid_Size_{a}")
+        g *= int(v) if v not in (None, "") else 1
+    return g
+
+
+def _kname(r):
+    """The kernel's demangled name without the leading 'void rpl::'."""
+    nm = r["Kernel_Name"]
+    return nm.split("rpl::", 1)[1] if "rpl::" in nm else nm
+
+
+def _select(recs, order_key):
+    """{(key, workload): {grid: [rows]}} following PHASES and PROFILES."""
+    recs = sorted(recs, key=lambda r: int(r[order_key]))
+    phase, pi, tagged = PHASES[0][0], 0, []
+    for r in recs:
+        if pi + 1 < len(PHASES) and PHASES[pi + 1][1] in _kname(r):
+            pi += 1
+            phase = PHASES[pi][0]
+        tagged.append((phase, r))
+    out = {}
+    for key, wname, prefix, ph, gsel in PROFILES:
+        grids = {}
+        for p_, r in tagged:
+            if p_ == ph and _kname(r).startswith(prefix):
+                grids.setdefault(_grid(r), []).append(r)
+        if not grids:
+            continue
+        if gsel == "all":
+            out[(key, wname)] = grids
+            continue
+        g = (min(grids) if gsel == "min" else max(grids) if gsel == "max"
+             else max(grids, key=lambda k: len(grids[k])))
+        out[(key, wname)] = {g: grids[g]}
+    return out
+
+
+def rocprof_summary(d: str):
+    """Write profiles/<key>__<workload>.md, profiles/pmc_traffic.json and profiles/mfma_util__*.md from
+    the rocprofv3 runs of PROFILE_RUNS found under d."""
+    import statistics
+    from row_matmul_reduce_amd import synth
+    wls = {w.name: w for w in synth.WORKLOADS.values()}
+    cmds = PROFILE_RUNS
+    trace = _csv_rows(os.path.join(d, "trace"), "*kernel_trace.csv")
+    stats = _csv_rows(os.path.join(d, "trace"), "*kernel_stats.csv") or []
+    if trace is None:
+        raise SystemExit(f"no kernel trace under {d}/trace")
+    tsel = _select(trace, "Start_Timestamp")
+
+    def counter(sub, name):
+        rows = _csv_rows(os.path.join(d, sub), "*counter_collection.csv")
+        return [r for r in rows if r["Counter_Name"] == name] if rows else None
+
+    fetch, write = counter("fetch", "FETCH_SIZE"), counter("write", "WRITE_SIZE")
+    cf, cw = counter("cal_fetch", "FETCH_SIZE"), counter("cal_write", "WRITE_SIZE")
+    traffic, rf, wf = None, None, None
+    if fetch and write and cf and cw:
+        cbytes = 512 << 20
+        fk = statistics.median(float(r["Counter_Value"]) for r in cf if "copy" in r["Kernel_Name"].lower())
+        wk = statistics.median(float(r["Counter_Value"]) for r in cw if "copy" in r["Kernel_Name"].lower())
+        rf, wf = cbytes / (fk * 1024), cbytes / (wk * 1024)
+        fsel, wsel = _select(fetch, "Dispatch_Id"), _select(write, "Dispatch_Id")
+        traffic = {"_about": "HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes (KiB per "
+                             "dispatch, median over the dispatches of the kernel at its workload), each scaled by what the "
+                             "same counter reads for a plain 512 MiB device copy: bytes = FETCH_SIZE*1024*read_factor + "
+                             "WRITE_SIZE*1024*write_factor.",
+                   "_copy_calibration": {"bytes": cbytes, "fetch_kib": fk, "write_kib": wk, "read_factor": rf,
+                                         "write_factor": wf},
+                   "_commands": [cmds["fetch"], cmds["write"], cmds["cal_fetch"], cmds["cal_write"]]}
+    lines_out = []
+    for key, wname, prefix, ph, gsel in PROFILES:
+        if (key, wname) not in tsel:
+            continue
+        w = wls[wname]
+        src_key = KERNEL_KEY.get(key, key)
+        sha = kernel_source_hash(src_key)
+        ab = _profile_alg_bytes(key, w)
+        md = [f"# {key} -- {wname}" + (f" ({PROFILE_NOTES[key]})" if key in PROFILE_NOTES else ""), "",
+              f"Workload: m={w.m} tokens, K_full={w.k_full} over TP={w.tp} (K_shard={w.k_shard}), n={w.n}, "
+              f"m_chunk={w.m_chunk}; kernel sources sha256/16 {sha}.", "",
+              "Command (kernel trace + stats; the bench cycles through HBM-resident input copies), then "
+              "`python bench.py --rocprof-summary <dir>`:", "", "    " + cmds["trace"], ""]
+        for g, sel in sorted(tsel[(key, wname)].items()):
+            durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in sel]
+            mean, med = statistics.mean(durs), statistics.median(durs)
+            if key.startswith("partial") and w.m_pad > 16:
+                rate = f"{w.gemm_flops() / (mean * 1e-6) / 1e12:.1f} T{'OP' if 'w8a8' in key else 'FLOP'}/s on the mean"
+            else:
+                rate = f"{ab / (mean * 1e-6) / 1e9:.0f} GB/s on the mean ({ab / 1e6:.2f} MB algorithmic)"
+            full = sel[0]["Kernel_Name"]
+            md += [f"Kernel `{full}`, grid {g} threads: {len(sel)} dispatches in the phase; duration mean {mean:.2f} us, "
+                   f"median {med:.2f} us, min {min(durs):.2f} us, max {max(durs):.2f} us; {rate}.", ""]
+            lines_out.append(f"{key:22s} {wname:28s} grid {g:8d} n={len(sel):6d} mean {mean:9.2f} us median {med:9.2f}")
+            st = [x for x in stats if x["Name"] == full]
+            if st:
+                x = st[0]
+                md += ["rocprofv3 --stats row of this kernel (every dispatch of it in the run, all phases):", "",
+                       '    "Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"',
+                       "    " + ",".join([f'"{x["Name"]}"'] + [x[c] for c in ("Calls", "TotalDurationNs", "AverageNs",
+                                                                          "Percentage", "MinNs", "MaxNs", "StdDev")]), ""]
+        if traffic is not None and (key, wname) in fsel and (key, wname) in wsel and gsel != "all":
+            fr = next(iter(fsel[(key, wname)].values()))
+            wr = next(iter(wsel[(key, wname)].values()))
+            fv = statistics.median(float(r["Counter_Value"]) for r in fr)
+            wv = statistics.median(float(r["Counter_Value"]) for r in wr)
+            hbm = fv * 1024 * rf + wv * 1024 * wf
+            traffic[f"{key}@{wname}"] = {"source_sha256_16": sha, "sources": KERNEL_SOURCES[src_key],
+                                         "kernel": fr[0]["Kernel_Name"], "dispatches": [len(fr), len(wr)],
+                                         "fetch_kib": fv, "write_kib": wv, "hbm_bytes_per_launch": hbm,
+                                         "algorithmic_bytes": ab, "ratio_to_algorithmic": hbm / ab}
+            md += [f"HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE, in separate runs of the bench; scaled by a "
+                   f"512 MiB device copy, read factor {rf:.3f}, write factor {wf:.3f}):", "",
+                   f"    FETCH_SIZE {fv:,.0f} KiB, WRITE_SIZE {wv:,.0f} KiB per dispatch (median of {len(fr)}) -> "
+                   f"{hbm / 1e6:.2f} MB per launch vs {ab / 1e6:.2f} MB algorithmic ({hbm / ab:.2f}x)", "",
+                   "    counter commands:"] + ["    " + c for c in traffic["_commands"]]
+        with open(os.path.join(ROOT, "profiles", f"{key}__{wname}.md"), "w") as f:
+            f.write("\n".join(md) + "\n")
+    if traffic is not None:
+        with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as f:
+            json.dump(traffic, f, indent=1)
+    print("\n".join(lines_out))
+    _mfma_summary(d, cmds["mfma"])
+
+
+def _mfma_summary(d, cmd):
+    import statistics
+    rows = _csv_rows(os.path.join(d, "mfma"), "*counter_collection.csv")
+    if not rows:
+        return
+    by = {}
+    for r in rows:
+        by.setdefault(int(r["Dispatch_Id"]), {"r": r})[r["Counter_Name"]] = float(r["Counter_Value"])
+    disp = [v for _, v in sorted(by.items())]
+    phase, pi, groups = PHASES[0][0], 0, {}
+    for dd in disp:
+        r = dd["r"]
+        if pi + 1 < len(PHASES) and PHASES[pi + 1][1] in _kname(r):
+            pi += 1
+            phase = PHASES[pi][0]
+        nm = r["Kernel_Name"]
+        if phase in ("prefill", "long") and "gemm_bf16_wide_kernel" in nm and _grid(r) == 65536:
+            label = f"`{_kname(r).split('(')[0]}` ({'prefill' if phase == 'prefill' else 'long prefill'}, grid 65536)"
+        elif phase == "w8a8" and "gemm_w8a8_wide_kernel" in nm and _grid(r) == 65536:
+            label = f"`{_kname(r).split('(')[0]}` (w8a8 prefill, grid 65536)"
+        elif phase in ("prefill", "long") and "Cijk_" in nm:
+            label = f"hipBLASLt `{nm[:20]}...` ({'prefill' if phase == 'prefill' else 'long prefill'}, same operands, grid {_grid(r)})"
+        else:
+            continue
+        groups.setdefault(label, []).append(dd)
+    out = ["# MFMA utilisation and clock -- bf16 and w8a8 partials on the prefill shares, and hipBLASLt on the same "
+           "operands", "", "Command (one counter pass; the bench cycles through HBM-resident input copies), then "
+           "`python bench.py --rocprof-summary <dir>`:", "", "    " + cmd, "",
+           "Per dispatch, medians over the dispatches of each kernel in its phase of the bench. "
+           "`SQ_VALU_MFMA_BUSY_CYCLES` is summed over the 1024 SIMDs, `GRBM_GUI_ACTIVE` over the 8 XCDs, so the "
+           "clock is `GUI_ACTIVE / 8 / duration` and the MFMA busy fraction `MFMA_BUSY / (1024 * GUI_ACTIVE / 8)`. "
+           "Counter collection serialises dispatches: durations are those of a kernel running alone.", "",
+           "| Kernel (workload) | Dispatches | Duration | MFMA_BUSY | GUI_ACTIVE | Clock | MFMA busy |",
+           "|---|---|---|---|---|---|---|"]
+    for label, ds in groups.items():
+        def med(k):
+            return statistics.median(x.get(k, float("nan")) for x in ds)
+        r0 = ds[0]["r"]
+        dur = None
+        if r0.get("Start_Timestamp"):
+            dur = statistics.median((int(x["r"]["End_Timestamp"]) - int(x["r"]["Start_Timestamp"])) / 1e3 for x in ds)
+        busy, gui = med("SQ_VALU_MFMA_BUSY_CYCLES"), med("GRBM_GUI_ACTIVE")
+        clk = f"{gui / 8 / (dur * 1e-6) / 1e9:.2f} GHz" if dur else "n/a"
+        durs = f"{dur:.1f} us" if dur else "n/a"
+        out.append(f"| {label} | {len(ds)} | {durs} | {busy:.4g} | {gui:.4g} | {clk} | {busy / (1024 * gui / 8):.0%} |")
+    with open(os.path.join(ROOT, "profiles", "mfma_util__prefill_down_proj_7b.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out[-len(groups):]))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -694,7 +958,12 @@ def main():
                     help="input sets cycled through (0: enough to exceed twice the 256 MB MALL)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy three times (scales HBM counters)")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="no GPU work: write profiles/ from the rocprofv3 runs of PROFILE_RUNS under DIR")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path is one tensor-parallel rank's share on one GPU (the "

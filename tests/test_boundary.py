@@ -455,7 +455,9 @@ def test_fused_noalloc_validation():
         (dict(xs=[X0.ptr, None]), NULL), (dict(res=None), NULL), (dict(gam=None), NULL), (dict(ro=None), NULL),
         (dict(m=-1), INVALID), (dict(mv=5), INVALID), (dict(n=0), INVALID), (dict(ldw=24), INVALID),
         (dict(eps=-1.0), INVALID), (dict(y=R.ptr), INVALID), (dict(ro=Y.ptr), INVALID),
-        (dict(n=60), UNSUP), (dict(m=65, mv=4), UNSUP), (dict(y=Y.ptr + 8), UNSUP),
+        (dict(n=60), UNSUP), (dict(y=Y.ptr + 8), UNSUP),
+        # m > 64 (fake device pointers far apart, so no overlap check fires first)
+        (dict(m=65, mv=4, res=1 << 40, y=1 << 41, ro=1 << 42), UNSUP),
         # hand-off memory of 4,352 + 4 * 64 * 2 * 8192 bytes > 4 MiB (fake device pointers: refused first)
         (dict(m=64, mv=0, n=8192, res=1 << 40, y=1 << 41, ro=1 << 42, gam=1 << 43), UNSUP),
     ]
