@@ -12,7 +12,7 @@
 //
 // Two kernels:
 //  * prefill: the four-wave form of the MFMA tile engine of gemm_nt.h
-//    (256 x 224 tiles, operands DMA'd straight to LDS, double-buffered) with
+//    (256 x 224 or 256 x 256 tiles, operands DMA'd straight to LDS, double-buffered) with
 //    v_mfma_f32_16x16x32_bf16 and fp32 accumulators in accumulation registers;
 //  * decode (M_pad <= 16): the weight stream dominates (a few tokens against
 //    the whole weight), so each workgroup owns 16 output columns, its waves
@@ -46,7 +46,7 @@ struct Bf16Op {
 template <int BN, int PF, bool KTAIL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (256 + BN) * KT_BYTES + PF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[wide_main_bytes(BN) + PF_BYTES];
     Bf16Op op{out, g.n};
     gemm_nt_wide<BN, PF, KTAIL>(g, op, smem);  // not staged: no staging area
 }
@@ -139,11 +139,22 @@ hipError_t launch_partial_bf16(const uint16_t *x, int64_t ldx, const uint16_t *w
     }
     GemmShape g{reinterpret_cast<const uint8_t *>(x), reinterpret_cast<const uint8_t *>(w),
                 ldx * 2, ldw * 2, m, m_pad, n, k * 2, 4};
-    const int nt = ((m_pad + 255) / 256) * ((n + 223) / 224);
-    if (g.kbytes % KT_BYTES)
-        hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, true>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
-    else
-        hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, false>), dim3(persistent_grid(nt)), dim3(256), 0, st, g, out);
+    // Tile width: each round of tiles (one per CU) costs about the tile's width, so take the width
+    // with the fewer rounds x width.  224 gives the prefill share 256 tiles (one round, where 256-wide
+    // tiles would leave 32 CUs idle); 256 gives the long-prefill share exactly five rounds instead of
+    // 5.75 (408 against 425 us on one box, bit-identical outputs).
+    // The 256-wide form is used without a K tail only (its per-lane tail cuts would spill registers).
+    const int tm = (m_pad + 255) / 256;
+    const int nt224 = tm * ((n + 223) / 224), nt256 = tm * ((n + 255) / 256);
+    const bool tail = g.kbytes % KT_BYTES;
+    const bool wide256 =
+        !tail && (int64_t)((nt256 + NUM_CU - 1) / NUM_CU) * 256 < (int64_t)((nt224 + NUM_CU - 1) / NUM_CU) * 224;
+    if (wide256) {
+        hipLaunchKernelGGL((gemm_bf16_wide_kernel<256, 3, false>), dim3(persistent_grid(nt256)), dim3(256), 0, st, g, out);
+    } else {
+        if (tail) hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, true>), dim3(persistent_grid(nt224)), dim3(256), 0, st, g, out);
+        else hipLaunchKernelGGL((gemm_bf16_wide_kernel<224, 3, false>), dim3(persistent_grid(nt224)), dim3(256), 0, st, g, out);
+    }
     return hipGetLastError();
 }
 

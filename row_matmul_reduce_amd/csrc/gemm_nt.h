@@ -111,6 +111,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
 
 constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 
+// LDS bytes of the engine's operand ring (two K steps of a 256 x BN tile) or, when larger, of the
+// row-major copy a finished tile is stored through (rows padded by 16 bytes); the prefetch sink and
+// any staging area follow it.
+__host__ __device__ constexpr int wide_main_bytes(int bn) {
+    return 2 * (256 + bn) * KT_BYTES > 256 * (bn * 2 + 16) ? 2 * (256 + bn) * KT_BYTES : 256 * (bn * 2 + 16);
+}
+
 // The engine: a 256 x BN tile (BN = 224 or 256) on 2 x 2 waves, 128 x BN/2
 // outputs per wave.  Per MFMA it reads a third fewer fragments from LDS than an
 // 8-wave layout (16 fragment reads feed 64 MFMAs instead of 8 feeding 16), and
@@ -154,7 +161,7 @@ constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
 // (long-prefill share: 429.1 -> 417.9 us against the direct store overlapped with those
 // DMAs).  Staged Ops take this path only for the last tile and only when coalesced_final()
 // (a second copy of it pushes the int8 kernel's registers into spills).
-// smem: 2 * (256 + BN) * KT_BYTES + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
+// smem: wide_main_bytes(BN) + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
 // staged Op.  KTAIL: K is not a whole number of steps (kbytes % KT_BYTES != 0), so the
 // last step's chunks past K are cut lane by lane; without a tail only whole steps past
 // the end are cut, by one uniform test per step, and the DMA addressing needs no
@@ -180,7 +187,8 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     const int nt_m = (g.m_pad + BM - 1) / BM, nt_n = (g.n + BN - 1) / BN;
     const int total = nt_m * nt_n;
     const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
-    uint8_t *const s0 = smem, *const s1 = smem + BUF, *const sink = smem + 2 * BUF;
+    constexpr int MAIN = wide_main_bytes(BN);
+    uint8_t *const s0 = smem, *const s1 = smem + BUF, *const sink = smem + MAIN;
     const int lr = lane >> 3;
     const int pc = (lane & 7) ^ lr;
     const int frow = lane & 15, fchunk = lane >> 4;
@@ -292,7 +300,7 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     // LDS at the start of each tile (Op::stage), so the epilogue reads LDS instead of
     // waiting on global loads behind the next tile's DMA.  Two areas alternate by tile:
     // a tile's staging never lands where the previous tile's epilogue still reads.
-    float *const stage_area = reinterpret_cast<float *>(smem + 2 * BUF + PF_BYTES);
+    float *const stage_area = reinterpret_cast<float *>(smem + MAIN + PF_BYTES);
     auto store_tile = [&](int m0, int n0, int par) {
         constexpr int LAST = (NR - 1) * NM / NR;  // first MFMA of the last group
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
@@ -322,7 +330,7 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     auto store_tile_lds = [&](int m0, int n0, int p) {
         constexpr int ROWB = BN * 2 + 16;  // tile row in LDS, padded so that 16 rows fall on distinct banks
         constexpr int CPR = BN / 8;        // 16-byte chunks per tile row
-        static_assert(BM * ROWB <= 2 * BUF, "the tile fits the operand buffers");
+        static_assert(BM * ROWB <= MAIN, "the tile copy fits the engine's LDS");
         constexpr int LAST = (NR - 1) * NM / NR;
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[LAST / FN][LAST % FN]));
 #pragma unroll

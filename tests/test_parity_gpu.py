@@ -53,6 +53,8 @@ SMALL_SHAPES = [
     (4100, 4104, 272, 2),  # 17 x 19 = 323 tiles > 256 workgroups: some run two; ragged m, n, K; 3 K steps
     (8192, 3584, 128, 2),  # 512 tiles of 256 x 224: every workgroup runs two tiles of one K step
     (4100, 4480, 256, 2),  # 17 x 20 = 340 tiles, some workgroups run two; 2 K steps per tile
+    (9211, 1784, 512, 2),  # 36 x 7 = 252 tiles of 256 x 256 (one round, where 256 x 224 needs two):
+                           # the 256-wide engine with ragged rows and columns
 ]
 
 
