@@ -716,7 +716,7 @@ PROFILES = [
     ("partial_bf16", "decode_o_proj_7b", "gemm_bf16_decode_kernel<2>", "decode", None),
     ("reduce_rmsnorm", "decode_o_proj_7b", "reduce_rmsnorm_kernel<", "decode", None),
     ("read_ceiling", "decode_o_proj_7b", "read_ceiling_kernel", "ceiling", "all"),
-    ("partial_bf16", "long_prefill_tp8_share", "gemm_bf16_wide_kernel<224, 3, false>", "long", None),
+    ("partial_bf16", "long_prefill_tp8_share", "gemm_bf16_wide_kernel<256, 3, false>", "long", None),
     ("reduce_rmsnorm", "long_prefill_tp8_share", "reduce_rmsnorm_kernel<", "long", None),
     ("decode_fused_chunk", "decode_o_proj_7b", "decode_fused_kernel<1, 4>", "fused", None),
     ("decode_fused_allrows", "decode_o_proj_7b", "decode_fused_kernel<1, 2>", "fused", None),

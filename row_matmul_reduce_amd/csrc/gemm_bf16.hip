@@ -13,7 +13,9 @@
 // Two kernels:
 //  * prefill: the four-wave form of the MFMA tile engine of gemm_nt.h
 //    (256 x 224 or 256 x 256 tiles, operands DMA'd straight to LDS, double-buffered) with
-//    v_mfma_f32_16x16x32_bf16 and fp32 accumulators in accumulation registers;
+//    v_mfma_f32_16x16x32_bf16 and fp32 accumulators in accumulation registers; the
+//    output goes out with streaming stores, so it does not sit dirty in the memory-side
+//    cache when the chunk reduce streams its inputs;
 //  * decode (M_pad <= 16): the weight stream dominates (a few tokens against
 //    the whole weight), so each workgroup owns 16 output columns, its waves
 //    split K, every wave issues all of its weight loads before its first MFMA,
@@ -37,9 +39,9 @@ struct Bf16Op {
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     }
     __device__ static __forceinline__ u32x2 pack(Acc v) { return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}; }
-    __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const { st8(out + (int64_t)mrow * n + ncol, pack(v)); }
+    __device__ __forceinline__ void store(Acc v, int mrow, int ncol) const { st8_nt(out + (int64_t)mrow * n + ncol, pack(v)); }
     // 8 consecutive output columns
-    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16(out + (int64_t)mrow * n + ncol, v); }
+    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16_nt(out + (int64_t)mrow * n + ncol, v); }
     __device__ static __forceinline__ bool coalesced_final() { return true; }
 };
 

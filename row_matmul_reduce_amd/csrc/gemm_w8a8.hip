@@ -45,11 +45,11 @@ struct W8a8Op {
         return u32x2{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3])};
     }
     __device__ __forceinline__ void store_staged(Acc v, int mrow, int ncol, float s, f32x4 w) const {
-        st8(out + (int64_t)mrow * n + ncol, pack_staged(v, s, w));
-        if (acc_out) st16(acc_out + (int64_t)mrow * n + ncol, __builtin_bit_cast(u32x4, v));
+        st8_nt(out + (int64_t)mrow * n + ncol, pack_staged(v, s, w));
+        if (acc_out) st16_nt(acc_out + (int64_t)mrow * n + ncol, __builtin_bit_cast(u32x4, v));
     }
     // 8 consecutive bf16 output columns
-    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16(out + (int64_t)mrow * n + ncol, v); }
+    __device__ __forceinline__ void store16(int mrow, int ncol, u32x4 v) const { st16_nt(out + (int64_t)mrow * n + ncol, v); }
     // the last tile goes through LDS unless the int32 accumulators are stored as well
     __device__ __forceinline__ bool coalesced_final() const { return acc_out == nullptr; }
     // DMA the token scales of tile rows m0 .. m0+255 (wave 0) and the channel scales of

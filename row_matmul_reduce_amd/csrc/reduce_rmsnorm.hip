@@ -33,7 +33,8 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int CPL, int RW, int ROWS>
+// NT: streaming stores for both outputs (chunks of many rows; see st16_nt).
+template <int CPL, int RW, int ROWS, bool NT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * RW * ROWS, 64 * RW * ROWS)))
 reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t *__restrict__ residual,
                       const uint16_t *__restrict__ gamma, float eps, uint16_t *y, uint16_t *residual_out) {
@@ -113,16 +114,21 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
                 ro[q] = pack_bf16x2(a, b);
                 yo[q] = pack_bf16x2(bf16_lo(gv[j][q]) * (a * inv), bf16_hi(gv[j][q]) * (b * inv));
             }
-            st16(residual_out + rbase + c * 8, ro);
-            st16(y + rbase + c * 8, yo);
+            if constexpr (NT) {
+                st16_nt(residual_out + rbase + c * 8, ro);
+                st16_nt(y + rbase + c * 8, yo);
+            } else {
+                st16(residual_out + rbase + c * 8, ro);
+                st16(y + rbase + c * 8, yo);
+            }
         }
     }
 }
 
-template <int CPL, int RW, int ROWS = 4 / RW>
+template <int CPL, int RW, bool NT, int ROWS = 4 / RW>
 static hipError_t launch_rr(const PartialPtrs &p, int tp, int m_chunk, int n, const uint16_t *residual,
                             const uint16_t *gamma, float eps, uint16_t *y, uint16_t *ro, hipStream_t st) {
-    hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPL, RW, ROWS>), dim3((m_chunk + ROWS - 1) / ROWS),
+    hipLaunchKernelGGL((reduce_rmsnorm_kernel<CPL, RW, ROWS, NT>), dim3((m_chunk + ROWS - 1) / ROWS),
                        dim3(64 * RW * ROWS), 0, st, p, tp, m_chunk, n, residual, gamma, eps, y, ro);
     return hipGetLastError();
 }
@@ -133,15 +139,20 @@ hipError_t launch_reduce_rmsnorm(const PartialPtrs &p, int tp, int m_chunk, int 
     // spread over 8 wavefronts (1-4 chunks per lane).  Many rows: one wavefront per row
     // (up to 8 chunks per lane, no cross-wave exchange), or 4 per row for rows wider than
     // 4096.  Measured on MI355X: decode chunk 3.8 -> 2.4 us, prefill chunk 15.1 -> 13.1 us.
+    // The many-row layouts write with streaming stores (long-prefill chunk after its partial
+    // product: 47 -> 43 us; prefill chunk 15.2 -> 14.2 us); the few-row one with ordinary ones.
     const int nch = n / 8;
-#define RR(C, W) \
-    case C: return launch_rr<C, W, 1>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
+#define RR(C, W, NT) \
+    case C: return launch_rr<C, W, NT, 1>(p, tp, m_chunk, n, residual, gamma, eps, y, ro, st);
     if (m_chunk < 512) {
-        switch ((nch + 511) / 512) { RR(1, 8) RR(2, 8) RR(3, 8) RR(4, 8) }
+        switch ((nch + 511) / 512) { RR(1, 8, false) RR(2, 8, false) RR(3, 8, false) RR(4, 8, false) }
     } else if (nch <= 64 * 8) {
-        switch ((nch + 63) / 64) { RR(1, 1) RR(2, 1) RR(3, 1) RR(4, 1) RR(5, 1) RR(6, 1) RR(7, 1) RR(8, 1) }
+        switch ((nch + 63) / 64) {
+            RR(1, 1, true) RR(2, 1, true) RR(3, 1, true) RR(4, 1, true)
+            RR(5, 1, true) RR(6, 1, true) RR(7, 1, true) RR(8, 1, true)
+        }
     } else {
-        switch ((nch + 255) / 256) { RR(3, 4) RR(4, 4) RR(5, 4) RR(6, 4) RR(7, 4) RR(8, 4) }
+        switch ((nch + 255) / 256) { RR(3, 4, true) RR(4, 4, true) RR(5, 4, true) RR(6, 4, true) RR(7, 4, true) RR(8, 4, true) }
     }
 #undef RR
     return hipErrorInvalidValue;

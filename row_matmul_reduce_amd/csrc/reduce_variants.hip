@@ -55,7 +55,7 @@ sum_partials_kernel(PartialPtrs P, int tp, int m, int n, int64_t ldp, uint16_t *
         u32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(h[2 * e], h[2 * e + 1]);
-        st16(out + row * n + col, o);
+        st16(out + row * n + col, o);  // its consumer reads it next: ordinary stores keep it cached
     }
 }
 
@@ -133,7 +133,7 @@ slice_sumsq_kernel(PartialPtrs P, int tp, int m, int ns, int64_t ld, const uint1
             u32x4 ro;
 #pragma unroll
             for (int q = 0; q < 4; ++q) ro[q] = pack_bf16x2(h[j][2 * q], h[j][2 * q + 1]);
-            st16(residual_out + rbase + c * 8, ro);
+            st16_nt(residual_out + rbase + c * 8, ro);
             float *hp = hout + (int64_t)row * ns + c * 8;
             *reinterpret_cast<f32x4 *>(hp) = f32x4{h[j][0], h[j][1], h[j][2], h[j][3]};
             *reinterpret_cast<f32x4 *>(hp + 4) = f32x4{h[j][4], h[j][5], h[j][6], h[j][7]};
@@ -179,7 +179,7 @@ slice_apply_kernel(const float *__restrict__ hin, SumsqPtrs S, int tp, int m, in
                 const float h0 = hv[j][q >> 1][(q & 1) * 2], h1 = hv[j][q >> 1][(q & 1) * 2 + 1];
                 yo[q] = pack_bf16x2(bf16_lo(gv[j][q]) * (h0 * inv), bf16_hi(gv[j][q]) * (h1 * inv));
             }
-            st16(y + (int64_t)row * ld + c * 8, yo);
+            st16_nt(y + (int64_t)row * ld + c * 8, yo);
         }
     }
 }

@@ -45,7 +45,7 @@ token_rows_kernel(PartialPtrs src, int64_t ld, int rows_out, int n, int gather, 
 #pragma unroll
             for (int u = 0; u < TR_U; ++u) {
                 const int c = c0 + u * 256;
-                if (c < nch) st16(op + c * 8, v[u]);
+                if (c < nch) st16_nt(op + c * 8, v[u]);
             }
         }
     }
