@@ -59,11 +59,11 @@ def test_rocprof_phase_selection():
     """The profile summariser splits the bench's dispatches into its phases by the first kernel of
     each phase and picks each profile's kernel by its full name (template arguments included):
     the decode step's rank partial is the 8-row kernel, not the peer chunk's 4-row one."""
-    names = ["gemm_bf16_wide_kernel<224, 3, false>(x)", "reduce_rmsnorm_kernel<7, 1, 1>(x)",
+    names = ["gemm_bf16_wide_kernel<224, 3, false>(x)", "reduce_rmsnorm_kernel<7, 1, 1, true>(x)",
              "gemm_w8a8_wide_kernel<224, 3, false>(x)", "quant_rows_kernel<4, 1, 1>(x)",
              "gemm_bf16_decode_kernel<4>(x)", "gemm_bf16_decode_kernel<2>(x)", "gemm_bf16_decode_kernel<2>(x)",
-             "reduce_rmsnorm_kernel<2, 8, 1>(x)", "read_ceiling_kernel(x)", "read_ceiling_kernel(x)",
-             "gemm_bf16_wide_kernel<224, 3, false>(x)", "reduce_rmsnorm_kernel<3, 4, 1>(x)",
+             "reduce_rmsnorm_kernel<2, 8, 1, false>(x)", "read_ceiling_kernel(x)", "read_ceiling_kernel(x)",
+             "gemm_bf16_wide_kernel<256, 3, false>(x)", "reduce_rmsnorm_kernel<3, 4, 1, true>(x)",
              "decode_fused_kernel<1, 4>(x)", "gemm_bf16_decode_kernel<4>(x)", "decode_fused_kernel<1, 2>(x)",
              "sum_partials_kernel(x)", "token_rows_kernel(x)", "token_rows_kernel(x)"]
     grids = [65536, 2048, 65536, 1024, 57344, 57344, 57344, 1024, 65536, 131072, 65536, 512, 115712, 57344,
@@ -75,7 +75,7 @@ def test_rocprof_phase_selection():
     assert list(dec) == [57344] and len(dec[57344]) == 2 and all("<2>" in r["Kernel_Name"] for r in dec[57344])
     assert list(sel[("partial_bf16", "prefill_down_proj_7b")][65536])[0]["Start_Timestamp"] == "0"
     assert sel[("partial_bf16", "long_prefill_tp8_share")][65536][0]["Start_Timestamp"] == "10"
-    assert "<3, 4, 1>" in sel[("reduce_rmsnorm", "long_prefill_tp8_share")][512][0]["Kernel_Name"]
+    assert "<3, 4, 1, true>" in sel[("reduce_rmsnorm", "long_prefill_tp8_share")][512][0]["Kernel_Name"]
     assert sorted(sel[("read_ceiling", "decode_o_proj_7b")]) == [65536, 131072]
     assert "<1, 4>" in sel[("decode_fused_chunk", "decode_o_proj_7b")][115712][0]["Kernel_Name"]
     assert list(sel[("token_rows_gather", "long_prefill_tp8_share")]) == [8192]
