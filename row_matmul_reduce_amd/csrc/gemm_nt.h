@@ -130,9 +130,13 @@ __host__ __device__ constexpr int wide_main_bytes(int bn) {
 // Per step: 128 bytes of K per row, double-buffered, DMA of step k+2 into the
 // buffer released by step k's barrier, L2 prefetch of step k+PF.  The interleave
 // is explicit rather than requested from the scheduler: each half-step is cut
-// into FM+FN groups of MFMAs, each followed by one fragment read of the other
-// half (and, in the second half, one DMA instruction), with a sched_barrier
-// after every group, so the issue order is exactly that.  Each wave issues 8 + FN DMA instructions per step (activation
+// into FM+FN groups of MFMAs, each followed by fragment reads of the other
+// half (two per group in the first half, one in the second) and, in the second
+// half, one DMA instruction, with a sched_barrier after every group, so the
+// issue order is exactly that.  (Against one read per group, activation
+// fragments first and a wait for all of them at the end of each half: prefill
+// share 199.8 -> 197.3 us, long-prefill share 396.2 -> 390.8 us on one box; in
+// cycles a little more, as the card then runs a slightly lower clock.)  Each wave issues 8 + FN DMA instructions per step (activation
 // groups wave, wave+4, ...; weight groups likewise), as many as it reads
 // fragments.  The K loop is unrolled by two so that the buffer addresses are
 // constants.
@@ -255,17 +259,24 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         const uint32_t off = isw ? (half ? fw1 : fw0) : (half ? fx1 : fx0);
         return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(buf + off + i * 16 * KT_BYTES));
     };
-    // One half-step: the MFMAs on (x, w) in NR groups; after group q, fragment q of the
-    // other set is read from rbuf (activation fragments first), and in the second half
-    // DMA instruction q of step dma_kt goes into dbuf.
+    // One half-step: the MFMAs on (x, w) in NR groups; after each group the next RP fragments
+    // of the other set are read from rbuf, weight fragments first (the next half's first MFMAs
+    // take all of them and the first activation fragment), and in the second half DMA
+    // instruction q of step dma_kt goes into dbuf.  The first half reads two fragments per group
+    // (RP = 2), so its reads are done by mid-half and the wait for them before the barrier
+    // finds them landed; the second half, whose DMAs share the groups, reads one per group.
     auto half = [&](const Frag *x, const Frag *w, Frag *lx, Frag *lw, const uint8_t *rbuf, int rhalf, bool with_dma,
                     int dma_kt, uint8_t *dbuf) {
+        const int RP = with_dma ? 1 : 2;  // a constant at each (inlined) call
 #pragma unroll
         for (int q = 0; q < NR; ++q) {
 #pragma unroll
             for (int i = q * NM / NR; i < (q + 1) * NM / NR; ++i) Op::mfma_acc(acc[i / FN][i % FN], w[i % FN], x[i / FN]);
-            if (q < FM) lx[q] = frag(rbuf, false, q, rhalf);
-            else lw[q - FM] = frag(rbuf, true, q - FM, rhalf);
+#pragma unroll
+            for (int r = q * RP; r < (q + 1) * RP && r < NR; ++r) {
+                if (r < FN) lw[r] = frag(rbuf, true, r, rhalf);
+                else lx[r - FN] = frag(rbuf, false, r - FN, rhalf);
+            }
             if (with_dma) dma(dma_kt, dbuf, q);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -292,8 +303,9 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         // Unconditional (one basic block): after the last step the reads fetch a buffer
         // nobody uses and the DMA offsets are out of range (zero fill of this wave's own
         // groups, ahead of its next tile's DMA into them).
+        // No wait here: each MFMA of the next half waits (in the compiler's counts) only for
+        // the fragments it takes, and the reads land in the order the MFMAs take them.
         half(xb, wb, xa, wa, nxt, 0, true, kt + 2, cur);
-        landed(xa, wa);
     };
     // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
     // Ops with per-row and per-column epilogue operands (Op::STAGED) have them DMA'd into
