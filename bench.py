@@ -698,6 +698,18 @@ PROFILE_RUNS = {
                  "python3 /root/repo/bench.py --copy-calibration",
     "mfma": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT -f csv "
             "-d <dir>/mfma -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    # memory-path and wait counters of the bf16 partials and hipBLASLt, three passes (each within the
+    # per-block counter limits of one pass)
+    "mem_a": "cd /tmp && rocprofv3 --pmc SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VMEM "
+             "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS -f csv -d <dir>/mem_a -o run -- "
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "mem_b": "cd /tmp && rocprofv3 --pmc TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum "
+             "TCP_PENDING_STALL_CYCLES_sum TCP_TCC_READ_REQ_sum TCP_TOTAL_CACHE_ACCESSES_sum GRBM_GUI_ACTIVE -f csv "
+             "-d <dir>/mem_b -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+    "mem_c": "cd /tmp && rocprofv3 --pmc SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE "
+             "SQ_ACTIVE_INST_LDS SQ_INST_LEVEL_VMEM SQ_INST_CYCLES_VMEM_RD SQ_INSTS_MFMA TA_DATA_STALLED_BY_TC_CYCLES_sum "
+             "TA_ADDR_STALLED_BY_TD_CYCLES_sum TD_TCP_STALL_CYCLES_sum TD_SPI_STALL_sum -f csv -d <dir>/mem_c -o run -- "
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
 }
 # The default run's phases, in order, each opened by the first dispatch whose name matches (after the
 # previous phase opened): the main bf16 prefill step, the two w8a8 steps, the decode step, the
@@ -892,6 +904,79 @@ def rocprof_summary(d: str):
             json.dump(traffic, f, indent=1)
     print("\n".join(lines_out))
     _mfma_summary(d, cmds["mfma"])
+    _memory_path_summary(d, cmds)
+
+
+def _counter_dispatches(d, sub):
+    """Per-dispatch counter dicts of one --pmc pass ({"r": first csv row, counter: value}), in dispatch
+    order, each tagged with its bench phase."""
+    rows = _csv_rows(os.path.join(d, sub), "*counter_collection.csv")
+    if not rows:
+        return None
+    by = {}
+    for r in rows:
+        by.setdefault(int(r["Dispatch_Id"]), {"r": r})[r["Counter_Name"]] = float(r["Counter_Value"])
+    phase, pi, out = PHASES[0][0], 0, []
+    for _, dd in sorted(by.items()):
+        if pi + 1 < len(PHASES) and PHASES[pi + 1][1] in _kname(dd["r"]):
+            pi += 1
+            phase = PHASES[pi][0]
+        out.append((phase, dd))
+    return out
+
+
+def _memory_path_summary(d, cmds, out_dir=None):
+    """profiles/memory_path_counters__prefill_down_proj_7b.md: per-dispatch medians of the memory-path
+    and wait counters for the bf16 partial and hipBLASLt on the prefill and long-prefill shares."""
+    import statistics
+    passes = [(k, _counter_dispatches(d, k)) for k in ("mem_a", "mem_b", "mem_c")]
+    if any(v is None for _, v in passes):
+        return
+    cols = [("lib:prefill", "prefill", "Cijk_"), ("lib:long", "long", "Cijk_"),
+            ("ours:prefill", "prefill", "gemm_bf16_wide_kernel"), ("ours:long", "long", "gemm_bf16_wide_kernel")]
+
+    def pick(disp, ph, key):
+        return [dd for p_, dd in disp if p_ == ph and key in dd["r"]["Kernel_Name"] and
+                (key == "Cijk_" or _grid(dd["r"]) == 65536)]
+
+    out = ["# Memory-path and wait counters -- bf16 partial (four-wave engine) against hipBLASLt, prefill down_proj "
+           "and long-prefill shares", "",
+           "Commands (three counter passes of the same bench command, each within the per-block counter limits of "
+           "one pass), then `python bench.py --rocprof-summary <dir>`:", ""]
+    out += ["    " + cmds[k] for k, _ in passes]
+    out += ["", "Per-dispatch medians. Columns: hipBLASLt (torch.matmul on the same operands) and the engine "
+            "(`gemm_bf16_wide_kernel`, its timed calls) on the prefill share (4096 x 9472 x 3584) and the long-prefill "
+            "share (16384 x 3200 x 5120). Durations are those of a kernel running alone (counter collection "
+            "serialises dispatches).", "", "```"]
+    waits = {}
+    for k, disp in passes:
+        sel = {c: pick(disp, ph, key) for c, ph, key in cols}
+        names = sorted({n for v in sel.values() for dd in v for n in dd if n != "r"})
+        out.append(f"== pass {k}")
+        out.append(f"{'counter':40s}" + "".join(f"{c:>16s}" for c, _, _ in cols))
+
+        def dur(v):
+            if not v or not v[0]["r"].get("Start_Timestamp"):
+                return float("nan")
+            return statistics.median((int(x["r"]["End_Timestamp"]) - int(x["r"]["Start_Timestamp"])) / 1e3 for x in v)
+        out.append(f"{'n / duration us':40s}" + "".join(f"{len(sel[c]):>7d}/{dur(sel[c]):8.1f}" for c, _, _ in cols))
+        for n in names:
+            vals = []
+            for c, _, _ in cols:
+                xs = [dd[n] for dd in sel[c] if n in dd]
+                vals.append(statistics.median(xs) if xs else float("nan"))
+                if n in ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"):
+                    waits.setdefault(c, {})[n] = vals[-1]
+            out.append(f"{n:40s}" + "".join(f"{v:16.4g}" for v in vals))
+    out.append("```")
+    if waits:
+        out += ["", "Fraction of wave cycles spent waiting (`SQ_WAIT_ANY / SQ_WAVE_CYCLES`): " + ", ".join(
+            f"{c} {w['SQ_WAIT_ANY'] / w['SQ_WAVE_CYCLES']:.1%}" for c, w in waits.items()
+            if w.get("SQ_WAVE_CYCLES"))]
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), "memory_path_counters__prefill_down_proj_7b.md"),
+              "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out[-3:]))
 
 
 def _mfma_summary(d, cmd):

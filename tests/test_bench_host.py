@@ -80,3 +80,34 @@ def test_rocprof_phase_selection():
     assert "<1, 4>" in sel[("decode_fused_chunk", "decode_o_proj_7b")][115712][0]["Kernel_Name"]
     assert list(sel[("token_rows_gather", "long_prefill_tp8_share")]) == [8192]
     assert list(sel[("token_rows_shard", "long_prefill_tp8_share")]) == [4096]
+
+
+def test_memory_path_summary(tmp_path):
+    """The memory-path counter summary takes each pass's per-dispatch rows, splits them into the bench's
+    phases and reports medians for hipBLASLt and the engine on both prefill shares."""
+    import csv
+    names = [("gemm_bf16_wide_kernel<224, 3, false>(x)", 65536), ("Cijk_lib_prefill", 57344),
+             ("gemm_w8a8_wide_kernel<224, 3, false>(x)", 65536), ("gemm_bf16_decode_kernel<2>(x)", 57344),
+             ("read_ceiling_kernel(x)", 65536), ("gemm_bf16_wide_kernel<256, 3, false>(x)", 65536),
+             ("Cijk_lib_long", 65536)]
+    counters = {"mem_a": ["SQ_WAIT_ANY", "SQ_WAVE_CYCLES"], "mem_b": ["TA_TA_BUSY_sum"],
+                "mem_c": ["TA_DATA_STALLED_BY_TC_CYCLES_sum"]}
+    for sub, cs in counters.items():
+        os.makedirs(tmp_path / sub)
+        with open(tmp_path / sub / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                              "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+            w.writeheader()
+            for i, (nm, g) in enumerate(names):
+                for j, c in enumerate(cs):
+                    kn = nm if nm.startswith("Cijk") else "void rpl::" + nm
+                    w.writerow({"Dispatch_Id": i, "Kernel_Name": kn, "Grid_Size": g, "Counter_Name": c,
+                                "Counter_Value": 10 * (i + 1) + j, "Start_Timestamp": 1000 * i,
+                                "End_Timestamp": 1000 * i + 500})
+    cmds = {k: f"cmd {k}" for k in counters}
+    bench._memory_path_summary(str(tmp_path), cmds, out_dir=str(tmp_path))
+    text = (tmp_path / "memory_path_counters__prefill_down_proj_7b.md").read_text()
+    row = next(ln for ln in text.splitlines() if ln.startswith("SQ_WAIT_ANY"))
+    # columns: lib prefill (dispatch 1), lib long (6), ours prefill (0), ours long (5)
+    assert [float(v) for v in row.split()[1:]] == [20.0, 70.0, 10.0, 60.0]
+    assert "cmd mem_b" in text and f"ours:long {60 / 61:.1%}" in text
