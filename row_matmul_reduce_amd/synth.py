@@ -177,8 +177,8 @@ def w8a8_inputs(wl: Workload, rows: int | None = None, shard: int = 0):
     xf = _rng(wl, T_XFP, shard).standard_normal((r, wl.k_shard), dtype=np.float32)
     absmax = np.max(np.abs(xf), axis=1)
     sx = (absmax / np.float32(127.0)).astype(np.float32)
-    sx = np.where(sx > 0, sx, np.float32(1.0)).astype(np.float32)
-    q = np.rint(xf / sx[:, None])
+    live = sx > 0  # an all-zero row (never drawn from N(0,1)) keeps scale 0 and codes 0
+    q = np.rint(xf / np.where(live, sx, np.float32(1.0))[:, None]) * live[:, None]
     xq = np.clip(q, -127, 127).astype(np.int8)
     wq, sw = w8a8_weight(wl, shard)
     return np.ascontiguousarray(xq), sx, wq, sw
