@@ -7,8 +7,8 @@
 // copy that the xLLM pull request #1890 "feat: add FlashComm1 and MMRS fusion
 // support for Qwen3.5 NPU" caches in its review thread; here it is not needed).
 //
-// One workgroup computes a 256 x 224 output tile with 2 x 2 wavefronts, 128 x 112
-// outputs per wave, the accumulators held in the accumulation registers.
+// One workgroup computes a 256 x 224 (or 256 x 256) output tile with 2 x 2 wavefronts,
+// 128 x 112 (128 x 128) outputs per wave, the accumulators held in the accumulation registers.
 //
 // Staging.  A K step stages 128 bytes of every operand row (64 bf16 or 128
 // int8 values) in LDS, double-buffered.  Rows reach LDS straight from memory
