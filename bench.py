@@ -495,6 +495,21 @@ def _dpm_files(torch):
     return {k: os.path.join(dev, f"pp_dpm_{k}") for k in ("sclk", "mclk")}
 
 
+def _hwmon_power(dpm_sclk_path):
+    """(power1_input path, power cap in W) of the card's hwmon, or (None, None) if not readable."""
+    import glob
+    dev = os.path.dirname(dpm_sclk_path)
+    for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+        p, c = os.path.join(h, "power1_input"), os.path.join(h, "power1_cap")
+        if os.path.exists(p) and os.access(p, os.R_OK):
+            try:
+                cap = int(open(c).read()) / 1e6 if os.path.exists(c) else None
+            except (OSError, ValueError):
+                cap = None
+            return p, cap
+    return None, None
+
+
 def _dpm_current_mhz(path):
     """MHz of the level marked current ('*') in a pp_dpm_* table."""
     try:
@@ -508,14 +523,18 @@ def _dpm_current_mhz(path):
     return None
 
 
-def clocks_under_load(torch, step, launches: int):
-    """SCLK and MCLK while `launches` steps run back to back: the current DPM level of the card,
-    read from sysfs every millisecond on a host thread (outside the timed region; same work)."""
+def clocks_under_load(torch, step, seconds: float = 1.5):
+    """SCLK, MCLK and board power while steps run back to back for `seconds`: the current DPM level
+    of the card and its hwmon power reading, read from sysfs every millisecond on a host thread
+    (outside the timed region; same work).  The power reading is a running average that takes a
+    good part of a second to settle, so only the samples of the second half of the window count."""
     import threading
     files = _dpm_files(torch)
     if files is None:
         return None
     samples = {"sclk": [], "mclk": []}
+    power_path, power_cap = _hwmon_power(files["sclk"])
+    watts = []
     stop = threading.Event()
 
     def sample():
@@ -524,20 +543,35 @@ def clocks_under_load(torch, step, launches: int):
                 v = _dpm_current_mhz(f)
                 if v is not None:
                     samples[k].append(v)
+            if power_path is not None:
+                try:
+                    watts.append(int(open(power_path).read()) / 1e6)
+                except (OSError, ValueError):
+                    pass
             time.sleep(0.001)
 
     th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
     th.start()
-    for i in range(launches):
-        step(i)
-    torch.cuda.synchronize()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     stop.set()
     th.join()
-    out = {"source": "current level of pp_dpm_sclk / pp_dpm_mclk, sampled every 1 ms while "
-                     f"{launches} steps ran", "card": os.path.dirname(files["sclk"])}
+    for v in list(samples.values()) + [watts]:
+        del v[:len(v) // 2]  # keep the settled second half
+    out = {"source": "current level of pp_dpm_sclk / pp_dpm_mclk and the hwmon power1_input, sampled every "
+                     f"1 ms while {i} steps ran back to back for {seconds:.1f} s; the second half of the "
+                     "samples", "card": os.path.dirname(files["sclk"])}
     for k, v in samples.items():
         out[f"{k}_mhz"] = ({"median": float(np.median(v)), "min": min(v), "max": max(v), "samples": len(v)}
                           if v else None)
+    out["power_w"] = ({"median": float(np.median(watts)), "min": min(watts), "max": max(watts), "samples": len(watts)}
+                      if watts else None)
+    out["power_cap_w"] = power_cap
     return out
 
 
@@ -602,10 +636,18 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
         theirs += timed(vendor)
     us, own = float(np.median(theirs)), float(np.median(ours))
     rate = wl.gemm_flops() / (us * 1e-6) / 1e12
+    # the card's clock and power while each GEMM runs back to back (outside the timed blocks)
+    load = {}
+    for name, fn in (("partial", path.partial), ("vendor", vendor)):
+        c = clocks_under_load(torch, lambda i, fn=fn: fn(path.sets[i % len(path.sets)]))
+        if c is not None:
+            load[name] = {"sclk_mhz": (c["sclk_mhz"] or {}).get("median"),
+                          "power_w": (c["power_w"] or {}).get("median"), "power_cap_w": c["power_cap_w"]}
     return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation; it and "
                     "the library's partial timed per launch in alternating blocks, medians",
             "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS,
-            "partial_us_same_method": own, "partial_over_vendor_time": own / us}
+            "partial_us_same_method": own, "partial_over_vendor_time": own / us,
+            "clock_and_power_under_load": load or None}
 
 
 def cpu_baseline(wl, budget_s: float, dynamic: bool = False):
@@ -1078,7 +1120,7 @@ def main():
     runner = path.run_graphs if small else path.run
     ms_per_step, kern, period = runner(args.steps, args.warmup)
     kernels = path.kernels_report(kern, period)
-    clocks = None if small else clocks_under_load(torch, path.step, 200)
+    clocks = None if small else clocks_under_load(torch, path.step)
     if not small:
         ru, rr = path.resident_partial_us()
         rate = "TFLOP/s" if not path.w8 else "TOP/s"
