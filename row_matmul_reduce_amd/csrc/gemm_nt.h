@@ -363,10 +363,23 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
                 *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = v;
             }
         __syncthreads();
-        for (int i = tid; i < BM * CPR; i += NW * 64) {
-            const int r = i / CPR, c = i - r * CPR;
-            if (m0 + r < g.m_pad && n0 + c * 8 < g.n)
-                op.store16(m0 + r, n0 + c * 8, *reinterpret_cast<const u32x4 *>(smem + r * ROWB + c * 16));
+        // Each thread stores PER chunks, in batches of SB whose LDS reads are all issued before
+        // the batch's stores, so a store never waits alone for its read.
+        constexpr int PER = BM * CPR / (NW * 64), SB = PER / 4;
+        static_assert(PER * NW * 64 == BM * CPR && SB * 4 == PER, "whole batches of chunks per thread");
+#pragma unroll 1
+        for (int b0 = 0; b0 < PER; b0 += SB) {
+            u32x4 v[SB];
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int i = tid + (b0 + u) * NW * 64, r = i / CPR, c = i - r * CPR;
+                v[u] = *reinterpret_cast<const u32x4 *>(smem + r * ROWB + c * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int i = tid + (b0 + u) * NW * 64, r = i / CPR, c = i - r * CPR;
+                if (m0 + r < g.m_pad && n0 + c * 8 < g.n) op.store16(m0 + r, n0 + c * 8, v[u]);
+            }
         }
         __syncthreads();  // every wave's reads of the copy have returned before LDS is reused
     };
