@@ -607,14 +607,19 @@ def token_rows(torch, rpl, copies: int):
 
 
 def library_reference(path, torch, rounds: int = 6, block: int = 20):
-    """Context only, not part of the path: the vendor GEMM (torch.matmul -> hipBLASLt) on the same
-    HBM-resident input sets.  It and the library's partial are timed the same way, per launch with
-    HIP events, in alternating blocks of `block` launches so both see the same clock; medians over
-    all launches.  Its result is not used anywhere."""
+    """Context only, not part of the path: the vendor GEMM on the same HBM-resident input sets --
+    torch.matmul (hipBLASLt, bf16) for the bf16 partial, torch._int_mm (hipBLASLt, int8 x int8 ->
+    int32, without the scales and with twice the output bytes) for the w8a8 partial.  It and the
+    library's partial are timed the same way, per launch with HIP events, in alternating blocks of
+    `block` launches so both see the same clock; medians over all launches.  Its result is not used
+    anywhere."""
     wl = path.wl
 
     def vendor(d):
-        torch.matmul(d["x"], d["w"].t())
+        if path.w8:
+            torch._int_mm(d["xq"], d["wq"].t())
+        else:
+            torch.matmul(d["x"], d["w"].t())
 
     def timed(fn):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(block)]
@@ -636,6 +641,12 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
         theirs += timed(vendor)
     us, own = float(np.median(theirs)), float(np.median(ours))
     rate = wl.gemm_flops() / (us * 1e-6) / 1e12
+    if path.w8:
+        return {"what": "torch._int_mm (hipBLASLt) of the same int8 operands, [m,k] x [n,k]^T -> int32 (no "
+                        "scales, 4-byte outputs); same input rotation; it and the library's w8a8 partial timed "
+                        "per launch in alternating blocks, medians",
+                "us": us, "TOP/s": rate, "frac_int8_peak": rate / PEAK_I8_TOPS,
+                "partial_us_same_method": own, "partial_over_vendor_time": own / us}
     # the card's clock and power while each GEMM runs back to back (outside the timed blocks)
     load = {}
     for name, fn in (("partial", path.partial), ("vendor", vendor)):
@@ -1163,7 +1174,7 @@ def main():
                 kp = side[key]["kernels"][sp.pname]
                 kp["plain_read_ceiling"] = ceil
                 kp["frac_of_ceiling"] = ceil["us"] / kp["us"]
-            if key == "long_prefill":
+            if key in ("long_prefill", "w8a8"):
                 side[key]["library_reference"] = library_reference(sp, torch)
             del sp
             torch.cuda.empty_cache()
