@@ -48,7 +48,7 @@ struct Bf16Op {
 template <int BN, int PF, bool KTAIL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_wide_kernel(GemmShape g, uint16_t *out) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[wide_main_bytes(BN) + PF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[wide_main_bytes(BN, false) + PF_BYTES];
     Bf16Op op{out, g.n};
     gemm_nt_wide<BN, PF, KTAIL>(g, op, smem);  // not staged: no staging area
 }

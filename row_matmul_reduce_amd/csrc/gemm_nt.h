@@ -11,7 +11,8 @@
 // 128 x 112 (128 x 128) outputs per wave, the accumulators held in the accumulation registers.
 //
 // Staging.  A K step stages 128 bytes of every operand row (64 bf16 or 128
-// int8 values) in LDS, double-buffered.  Rows reach LDS straight from memory
+// int8 values) in LDS: the activation double-buffered, the weight in a ring of
+// three steps where the LDS holds it (two otherwise).  Rows reach LDS straight from memory
 // with buffer_load_dwordx4 ... lds (no VGPR round trip): one wave instruction
 // fills 8 rows x 128 bytes.  The buffer descriptor of each operand starts at
 // the tile's first row and its record count ends at the operand's last valid
@@ -22,7 +23,8 @@
 // fall on distinct banks (zero bank conflicts measured with rocprofv3).
 //
 // L2 prefetch.  Two buffers of LDS give the DMA of step k+2 one step of lead,
-// less than the latency of HBM under load.  So each step also touches the
+// less than the latency of HBM under load.  The weight ring's third buffer gives
+// the weight DMA (step k+3) two; for the activation each step also touches the
 // lines of step k+PF (PF = 3) -- one 4-byte DMA per 128-byte line into a
 // 256-byte LDS sink that is never read -- so that the real DMA finds them in
 // L2.  The workgroups of an XCD that share activation rows split their
@@ -30,7 +32,8 @@
 // than once per sharer (half the L2 requests of a per-workgroup prefetch).
 // Only the activation is prefetched: the four workgroups of an XCD that share
 // a weight tile request its lines together anyway, and prefetching it as well
-// measured 2% slower.  The barrier waits for every load but the newest one.
+// measured 2% slower.  The barrier waits for every load but the newest prefetch
+// (and, with the weight ring, the weight DMAs of the step after next).
 //
 // MFMA operand roles are swapped (A <- weight rows, B <- activation rows) so
 // that each lane's 4 accumulators are 4 consecutive output columns of one
@@ -110,12 +113,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t *base,
 }
 
 constexpr int WIDE_STAGE_BYTES = 2 * (256 + 256) * 4;
+constexpr int LDS_BYTES = 160 * 1024;  // per workgroup on gfx950
 
-// LDS bytes of the engine's operand ring (two K steps of a 256 x BN tile) or, when larger, of the
-// row-major copy a finished tile is stored through (rows padded by 16 bytes); the prefetch sink and
-// any staging area follow it.
-__host__ __device__ constexpr int wide_main_bytes(int bn) {
-    return 2 * (256 + bn) * KT_BYTES > 256 * (bn * 2 + 16) ? 2 * (256 + bn) * KT_BYTES : 256 * (bn * 2 + 16);
+// Weight steps in the engine's LDS ring: three where they fit next to the activation's two, the
+// prefetch sink and (staged Ops) the staging area, else two.
+__host__ __device__ constexpr int wide_w_stages(int bn, bool staged) {
+    return (2 * 256 + 3 * bn) * KT_BYTES + PF_BYTES + (staged ? WIDE_STAGE_BYTES : 0) <= LDS_BYTES ? 3 : 2;
+}
+// LDS bytes of the engine's operand rings (two activation steps and wide_w_stages weight steps of a
+// 256 x BN tile) or, when larger, of the row-major copy a finished tile is stored through (rows
+// padded by 16 bytes); the prefetch sink and any staging area follow it.
+__host__ __device__ constexpr int wide_main_bytes(int bn, bool staged) {
+    return (2 * 256 + wide_w_stages(bn, staged) * bn) * KT_BYTES > 256 * (bn * 2 + 16)
+               ? (2 * 256 + wide_w_stages(bn, staged) * bn) * KT_BYTES
+               : 256 * (bn * 2 + 16);
 }
 
 // The engine: a 256 x BN tile (BN = 224 or 256) on 2 x 2 waves, 128 x BN/2
@@ -127,8 +138,10 @@ __host__ __device__ constexpr int wide_main_bytes(int bn) {
 // an "a"-constrained operand), which leaves the 256 vector registers to the two
 // fragment sets and the addressing.
 //
-// Per step: 128 bytes of K per row, double-buffered, DMA of step k+2 into the
-// buffer released by step k's barrier, L2 prefetch of step k+PF.  The interleave
+// Per step: 128 bytes of K per row, DMA of the activation's step k+2 (and of the weight's
+// step k+3 with a three-step ring, else k+2) into the buffers released by step k's barrier,
+// L2 prefetch of the activation's step k+PF.  (The third weight buffer: prefill share
+// 195.1 -> 192.3, 199.2 -> 195.7 and 195.2 -> 191.1 us on three boxes, bit-identical.)  The interleave
 // is explicit rather than requested from the scheduler: each half-step is cut
 // into FM+FN groups of MFMAs, each followed by fragment reads of the other
 // half (two per group in the first half, one in the second) and, in the second
@@ -138,8 +151,8 @@ __host__ __device__ constexpr int wide_main_bytes(int bn) {
 // share 199.8 -> 197.3 us, long-prefill share 396.2 -> 390.8 us on one box; in
 // cycles a little more, as the card then runs a slightly lower clock.)  Each wave issues 8 + FN DMA instructions per step (activation
 // groups wave, wave+4, ...; weight groups likewise), as many as it reads
-// fragments.  The K loop is unrolled by two so that the buffer addresses are
-// constants.
+// fragments.  The K loop is unrolled by two (six with a three-step weight ring) so
+// that the buffer addresses are constants.
 //
 // Hazards the compiler cannot see through inline assembly: zeroed accumulators
 // are written before the first MFMA reads them (a tie to each, then s_nop), and
@@ -165,8 +178,8 @@ __host__ __device__ constexpr int wide_main_bytes(int bn) {
 // (long-prefill share: 429.1 -> 417.9 us against the direct store overlapped with those
 // DMAs).  Staged Ops take this path only for the last tile and only when coalesced_final()
 // (a second copy of it pushes the int8 kernel's registers into spills).
-// smem: wide_main_bytes(BN) + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES for a
-// staged Op.  KTAIL: K is not a whole number of steps (kbytes % KT_BYTES != 0), so the
+// smem: wide_main_bytes(BN, Op::STAGED) + PF_BYTES bytes of LDS, plus WIDE_STAGE_BYTES
+// for a staged Op.  KTAIL: K is not a whole number of steps (kbytes % KT_BYTES != 0), so the
 // last step's chunks past K are cut lane by lane; without a tail only whole steps past
 // the end are cut, by one uniform test per step, and the DMA addressing needs no
 // vector instruction at all (2-3% faster on the prefill shares than the per-lane form).
@@ -180,7 +193,8 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     constexpr int NR = FM + FN, NM = FM * FN;          // fragment reads and MFMAs per half-step
     static_assert(GA % NW == 0 && GB % NW == 0 && NA + NB == NR, "one DMA per fragment read");
     static_assert(BM / PF_SHARE_X <= 64, "activation prefetch slice fits one wave");
-    constexpr int BUF = (BM + BN) * KT_BYTES;
+    constexpr int WS = wide_w_stages(BN, Op::STAGED);  // weight steps in the ring
+    constexpr int XB = BM * KT_BYTES, WB = BN * KT_BYTES;
     constexpr int STAGE_FLOATS = BM + 256;  // one staging area: a value per tile row and per column
     using Frag = typename Op::Frag;
     using Acc = typename Op::Acc;
@@ -191,8 +205,11 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     const int nt_m = (g.m_pad + BM - 1) / BM, nt_n = (g.n + BN - 1) / BN;
     const int total = nt_m * nt_n;
     const int ksteps = (g.kbytes + KT_BYTES - 1) / KT_BYTES;
-    constexpr int MAIN = wide_main_bytes(BN);
-    uint8_t *const s0 = smem, *const s1 = smem + BUF, *const sink = smem + MAIN;
+    constexpr int MAIN = wide_main_bytes(BN, Op::STAGED);
+    static_assert(MAIN + PF_BYTES + (Op::STAGED ? WIDE_STAGE_BYTES : 0) <= LDS_BYTES, "LDS budget");
+    uint8_t *const X0 = smem, *const X1 = smem + XB;                       // activation steps
+    uint8_t *const W0 = smem + 2 * XB, *const W1 = W0 + WB, *const W2 = W1 + WB;  // weight steps
+    uint8_t *const sink = smem + MAIN;
     const int lr = lane >> 3;
     const int pc = (lane & 7) ^ lr;
     const int frow = lane & 15, fchunk = lane >> 4;
@@ -200,26 +217,27 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     __amdgpu_buffer_rsrc_t rx, rw;
     TileSpan sx{}, sw{};  // the same tiles as base and record count (per-step descriptors)
     int pfx0 = 0;  // first row of this workgroup's activation prefetch slice
-    // DMA instruction j of step kt into buf: activation group j*NW + wave (j < NA), else
-    // weight group (j-NA)*NW + wave.  j is a compile-time constant at every call.
+    // DMA instruction j: activation group j*NW + wave of step ktx into xbuf (j < NA), else
+    // weight group (j-NA)*NW + wave of step ktw into wbuf.  j is a compile-time constant at
+    // every call.
     // With a K tail each lane's offset is cut to OOB_OFFSET past K.  Without one the
     // per-lane offset is the same at every step (the compiler keeps it in a register)
     // and the step's byte offset goes in the scalar offset; a step past the end gets a
     // descriptor with no records, so its loads read nothing.  Either way a lane's byte
     // is row * ld + k, inside the row's K bytes or out of range.
-    auto dma = [&](int kt, uint8_t *buf, int j) {
+    auto dma = [&](int ktx, uint8_t *xbuf, int ktw, uint8_t *wbuf, int j) {
+        const int kt = j < NA ? ktx : ktw;
         if constexpr (KTAIL) {
             const int kb = kt * KT_BYTES + pc * 16;
             const bool kin = kb < g.kbytes;
             if (j < NA) {
                 const int gi = j * NW + wave;
                 const uint32_t v = kin ? (uint32_t)((gi * 8 + lr) * g.ldx + kb) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(buf + gi * 1024), 16, v, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(xbuf + gi * 1024), 16, v, 0, 0, 0);
             } else {
                 const int gj = (j - NA) * NW + wave;
                 const uint32_t v = kin ? (uint32_t)((gj * 8 + lr) * g.ldw + kb) : OOB_OFFSET;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v,
-                                                         0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(wbuf + gj * 1024), 16, v, 0, 0, 0);
             }
         } else {
             const bool live = kt * KT_BYTES < g.kbytes;
@@ -227,14 +245,13 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
             if (j < NA) {
                 const int gi = j * NW + wave;
                 const uint32_t v = (uint32_t)((gi * 8 + lr) * g.ldx + pc * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sx, live), (lds_void_t *)(buf + gi * 1024), 16, v,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sx, live), (lds_void_t *)(xbuf + gi * 1024), 16, v,
                                                          kstep, 0, 0);
             } else {
                 const int gj = (j - NA) * NW + wave;
                 const uint32_t v = (uint32_t)((gj * 8 + lr) * g.ldw + pc * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sw, live),
-                                                         (lds_void_t *)(buf + BM * KT_BYTES + gj * 1024), 16, v, kstep,
-                                                         0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(span_rsrc(sw, live), (lds_void_t *)(wbuf + gj * 1024), 16, v,
+                                                         kstep, 0, 0);
             }
         }
     };
@@ -253,20 +270,20 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
     // of 8, has the same swizzle: one lane offset per operand and half, plus a constant.
     static_assert(TM % 8 == 0 && TN % 8 == 0, "fragment rows keep the swizzle of the first");
     const uint32_t fx0 = swz_off(wm0 + frow, fchunk), fx1 = swz_off(wm0 + frow, 4 + fchunk);
-    const uint32_t fw0 = BM * KT_BYTES + swz_off(wn0 + frow, fchunk);
-    const uint32_t fw1 = BM * KT_BYTES + swz_off(wn0 + frow, 4 + fchunk);
-    auto frag = [&](const uint8_t *buf, bool isw, int i, int half) -> Frag {
+    const uint32_t fw0 = swz_off(wn0 + frow, fchunk), fw1 = swz_off(wn0 + frow, 4 + fchunk);
+    auto frag = [&](const uint8_t *xbuf, const uint8_t *wbuf, bool isw, int i, int half) -> Frag {
         const uint32_t off = isw ? (half ? fw1 : fw0) : (half ? fx1 : fx0);
-        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>(buf + off + i * 16 * KT_BYTES));
+        return __builtin_bit_cast(Frag, *reinterpret_cast<const u32x4 *>((isw ? wbuf : xbuf) + off + i * 16 * KT_BYTES));
     };
     // One half-step: the MFMAs on (x, w) in NR groups; after each group the next RP fragments
-    // of the other set are read from rbuf, weight fragments first (the next half's first MFMAs
-    // take all of them and the first activation fragment), and in the second half DMA
-    // instruction q of step dma_kt goes into dbuf.  The first half reads two fragments per group
+    // of the other set are read from (rxb, rwb), weight fragments first (the next half's first
+    // MFMAs take all of them and the first activation fragment), and in the second half DMA
+    // instruction q of the activation's step dkt into dxb and of the weight's step dkt + WS - 2
+    // into dwb.  The first half reads two fragments per group
     // (RP = 2), so its reads are done by mid-half and the wait for them before the barrier
     // finds them landed; the second half, whose DMAs share the groups, reads one per group.
-    auto half = [&](const Frag *x, const Frag *w, Frag *lx, Frag *lw, const uint8_t *rbuf, int rhalf, bool with_dma,
-                    int dma_kt, uint8_t *dbuf) {
+    auto half = [&](const Frag *x, const Frag *w, Frag *lx, Frag *lw, const uint8_t *rxb, const uint8_t *rwb,
+                    int rhalf, bool with_dma, int dkt, uint8_t *dxb, uint8_t *dwb) {
         const int RP = with_dma ? 1 : 2;  // a constant at each (inlined) call
 #pragma unroll
         for (int q = 0; q < NR; ++q) {
@@ -274,10 +291,10 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
             for (int i = q * NM / NR; i < (q + 1) * NM / NR; ++i) Op::mfma_acc(acc[i / FN][i % FN], w[i % FN], x[i / FN]);
 #pragma unroll
             for (int r = q * RP; r < (q + 1) * RP && r < NR; ++r) {
-                if (r < FN) lw[r] = frag(rbuf, true, r, rhalf);
-                else lx[r - FN] = frag(rbuf, false, r - FN, rhalf);
+                if (r < FN) lw[r] = frag(rxb, rwb, true, r, rhalf);
+                else lx[r - FN] = frag(rxb, rwb, false, r - FN, rhalf);
             }
-            if (with_dma) dma(dma_kt, dbuf, q);
+            if (with_dma) dma(dkt, dxb, dkt + WS - 2, dwb, q);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -287,17 +304,19 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
 #pragma unroll
         for (int b = 0; b < FN; ++b) asm volatile("" ::"v"(wf[b]));
     };
+    // Waits for step kt+1: what may stay in flight is the newest prefetch and, with a three-step
+    // weight ring, the weight DMAs of step kt+2 (the last NB DMAs of the previous step).
+    constexpr int INFLIGHT = (PF > 0 ? 1 : 0) + (WS == 3 ? NB : 0);
     auto barrier = [&]() {
-        if (PF > 0) asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(INFLIGHT) : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Step kt reads buffer cur; step kt+1 lands in nxt; step kt+2's DMA goes into cur once
-    // every wave has passed this step's barrier.
-    auto kstep = [&](int kt, uint8_t *cur, uint8_t *nxt) {
+    // Step kt reads (xc, wc); step kt+1 lands in (xn, wn); the activation's step kt+2 goes into xc
+    // and the weight's step kt+WS into wc once every wave has passed this step's barrier.
+    auto kstep = [&](int kt, uint8_t *xc, uint8_t *wc, uint8_t *xn, uint8_t *wn) {
         if (PF > 0) prefetch(kt + PF);  // past the end: out of range, reads nothing
         __builtin_amdgcn_sched_barrier(0);
-        half(xa, wa, xb, wb, cur, 1, false, 0, nullptr);
+        half(xa, wa, xb, wb, xc, wc, 1, false, 0, nullptr, nullptr);
         landed(xb, wb);
         barrier();
         // Unconditional (one basic block): after the last step the reads fetch a buffer
@@ -305,7 +324,7 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         // groups, ahead of its next tile's DMA into them).
         // No wait here: each MFMA of the next half waits (in the compiler's counts) only for
         // the fragments it takes, and the reads land in the order the MFMAs take them.
-        half(xb, wb, xa, wa, nxt, 0, true, kt + 2, cur);
+        half(xb, wb, xa, wa, xn, wn, 0, true, kt + 2, xc, wc);
     };
     // Epilogue: lane holds out[m0+wm0+a*16+(lane&15)][n0+wn0+b*16+4*(lane>>4) + 0..3].
     // Ops with per-row and per-column epilogue operands (Op::STAGED) have them DMA'd into
@@ -409,13 +428,17 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         }
         for (int d = 2; d < PF; ++d) prefetch(d);
 #pragma unroll
-        for (int j = 0; j < NR; ++j) dma(0, s0, j);  // the previous tile's reads all ended at its barriers
+        for (int j = 0; j < NR; ++j) dma(0, X0, 0, W0, j);  // the previous tile's reads all ended at its barriers
         if (have_prev && !lds_store) {
             store_tile(pm0, pn0, par);
             par = 1 - par;
         }
 #pragma unroll
-        for (int j = 0; j < NR; ++j) dma(1, s1, j);  // out of range (zeros) when ksteps == 1
+        for (int j = 0; j < NR; ++j) dma(1, X1, 1, W1, j);  // out of range (zeros) past the last step
+        if constexpr (WS == 3) {
+#pragma unroll
+            for (int j = NA; j < NR; ++j) dma(0, X0, 2, W2, j);  // weight groups only
+        }
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -423,17 +446,28 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
                 acc[a][b] = Op::zero();
                 asm volatile("" : "+a"(acc[a][b]));
             }
-        // step 0 and the stores have landed (step 1's NR DMAs may still be in flight);
-        // the s_nop separates the accumulator writes from the first MFMA
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier\n\ts_nop 4" ::"n"(NR) : "memory");
+        // step 0 and the stores have landed (step 1's NR DMAs and the weight's step 2 may still
+        // be in flight); the s_nop separates the accumulator writes from the first MFMA
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier\n\ts_nop 4" ::"n"(NR + (WS == 3 ? NB : 0)) : "memory");
 #pragma unroll
-        for (int a = 0; a < FM; ++a) xa[a] = frag(s0, false, a, 0);
+        for (int a = 0; a < FM; ++a) xa[a] = frag(X0, W0, false, a, 0);
 #pragma unroll
-        for (int b = 0; b < FN; ++b) wa[b] = frag(s0, true, b, 0);
+        for (int b = 0; b < FN; ++b) wa[b] = frag(X0, W0, true, b, 0);
         landed(xa, wa);
-        for (int kt = 0; kt < ksteps; kt += 2) {
-            kstep(kt, s0, s1);
-            if (kt + 1 < ksteps) kstep(kt + 1, s1, s0);
+        if constexpr (WS == 3) {
+            for (int kt = 0; kt < ksteps; kt += 6) {
+                kstep(kt, X0, W0, X1, W1);
+                if (kt + 1 < ksteps) kstep(kt + 1, X1, W1, X0, W2);
+                if (kt + 2 < ksteps) kstep(kt + 2, X0, W2, X1, W0);
+                if (kt + 3 < ksteps) kstep(kt + 3, X1, W0, X0, W1);
+                if (kt + 4 < ksteps) kstep(kt + 4, X0, W1, X1, W2);
+                if (kt + 5 < ksteps) kstep(kt + 5, X1, W2, X0, W0);
+            }
+        } else {
+            for (int kt = 0; kt < ksteps; kt += 2) {
+                kstep(kt, X0, W0, X1, W1);
+                if (kt + 1 < ksteps) kstep(kt + 1, X1, W1, X0, W0);
+            }
         }
         pm0 = m0;
         pn0 = n0;

@@ -72,7 +72,7 @@ struct W8a8Op {
 template <int BN, int PF, bool KTAIL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256))) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_w8a8_wide_kernel(GemmShape g, W8a8Op op) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[wide_main_bytes(BN) + PF_BYTES + WIDE_STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[wide_main_bytes(BN, true) + PF_BYTES + WIDE_STAGE_BYTES];
     gemm_nt_wide<BN, PF, KTAIL>(g, op, smem);
 }
 
