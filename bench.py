@@ -953,11 +953,41 @@ def rocprof_summary(d: str):
         with open(os.path.join(ROOT, "profiles", f"{key}__{wname}.md"), "w") as f:
             f.write("\n".join(md) + "\n")
     if traffic is not None:
+        traffic.update(_vendor_traffic(d, wls, rf, wf))
         with open(os.path.join(ROOT, "profiles", "pmc_traffic.json"), "w") as f:
             json.dump(traffic, f, indent=1)
     print("\n".join(lines_out))
     _mfma_summary(d, cmds["mfma"])
     _memory_path_summary(d, cmds)
+
+
+def _vendor_traffic(d, wls, rf, wf):
+    """HBM traffic of the vendor GEMMs the bench times beside the partials (hipBLASLt's kernels, named
+    Cijk_*), from the same FETCH_SIZE / WRITE_SIZE passes and copy calibration as the library's
+    kernels, against the algorithmic bytes of the vendor's own problem (its int8 GEMM writes int32)."""
+    import statistics
+    fd, wd = _counter_dispatches(d, "fetch"), _counter_dispatches(d, "write")
+    out = {}
+    if not fd or not wd:
+        return out
+    for ph, wname, label in (("prefill", "prefill_down_proj_7b", "hipblaslt_bf16"),
+                             ("w8a8", "w8a8_prefill_down_proj_7b", "hipblaslt_int8"),
+                             ("long", "long_prefill_tp8_share", "hipblaslt_bf16")):
+        fr = [dd for p_, dd in fd if p_ == ph and "Cijk_" in dd["r"]["Kernel_Name"] and "FETCH_SIZE" in dd]
+        wr = [dd for p_, dd in wd if p_ == ph and "Cijk_" in dd["r"]["Kernel_Name"] and "WRITE_SIZE" in dd]
+        if not fr or not wr:
+            continue
+        w = wls[wname]
+        ab = (w.m * w.k_shard + w.n * w.k_shard + 4 * w.m * w.n) if label.endswith("int8") else \
+            2 * (w.m * w.k_shard + w.n * w.k_shard + w.m * w.n)
+        fv = statistics.median(dd["FETCH_SIZE"] for dd in fr)
+        wv = statistics.median(dd["WRITE_SIZE"] for dd in wr)
+        hbm = fv * 1024 * rf + wv * 1024 * wf
+        out[f"{label}@{wname}"] = {"kernel": fr[0]["r"]["Kernel_Name"][:120], "dispatches": [len(fr), len(wr)],
+                                   "fetch_kib": fv, "write_kib": wv, "hbm_bytes_per_launch": hbm,
+                                   "algorithmic_bytes": ab, "ratio_to_algorithmic": hbm / ab,
+                                   "note": "vendor GEMM on the same operands (context, not part of the path)"}
+    return out
 
 
 def _counter_dispatches(d, sub):

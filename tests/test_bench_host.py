@@ -111,3 +111,33 @@ def test_memory_path_summary(tmp_path):
     # columns: lib prefill (dispatch 1), lib long (6), ours prefill (0), ours long (5)
     assert [float(v) for v in row.split()[1:]] == [20.0, 70.0, 10.0, 60.0]
     assert "cmd mem_b" in text and f"ours:long {60 / 61:.1%}" in text
+
+
+def test_vendor_traffic(tmp_path):
+    """The vendor GEMMs' HBM traffic comes from the same FETCH_SIZE / WRITE_SIZE passes, picked by phase,
+    scaled by the copy calibration and set against the vendor problem's own algorithmic bytes."""
+    import csv
+    from row_matmul_reduce_amd import synth
+    names = [("gemm_bf16_wide_kernel<224, 3, false>(x)", 65536), ("Cijk_lib_prefill", 57344),
+             ("gemm_w8a8_wide_kernel<224, 3, false>(x)", 65536), ("Cijk_lib_int8", 57344),
+             ("gemm_bf16_decode_kernel<2>(x)", 57344), ("read_ceiling_kernel(x)", 65536),
+             ("gemm_bf16_wide_kernel<256, 3, false>(x)", 65536), ("Cijk_lib_long", 65536)]
+    for sub, c in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        os.makedirs(tmp_path / sub)
+        with open(tmp_path / sub / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                              "Counter_Value"])
+            w.writeheader()
+            for i, (nm, g) in enumerate(names):
+                kn = nm if nm.startswith("Cijk") else "void rpl::" + nm
+                w.writerow({"Dispatch_Id": i, "Kernel_Name": kn, "Grid_Size": g, "Counter_Name": c,
+                            "Counter_Value": 1000 * (i + 1) if c == "FETCH_SIZE" else 100 * (i + 1)})
+    wls = {wl.name: wl for wl in synth.WORKLOADS.values()}
+    got = bench._vendor_traffic(str(tmp_path), wls, 2.0, 1.0)
+    assert sorted(got) == ["hipblaslt_bf16@long_prefill_tp8_share", "hipblaslt_bf16@prefill_down_proj_7b",
+                           "hipblaslt_int8@w8a8_prefill_down_proj_7b"]
+    e = got["hipblaslt_int8@w8a8_prefill_down_proj_7b"]  # dispatch 3
+    assert e["hbm_bytes_per_launch"] == 4000 * 1024 * 2.0 + 400 * 1024 * 1.0
+    wl = wls["w8a8_prefill_down_proj_7b"]
+    assert e["algorithmic_bytes"] == wl.m * wl.k_shard + wl.n * wl.k_shard + 4 * wl.m * wl.n
+    assert got["hipblaslt_bf16@long_prefill_tp8_share"]["fetch_kib"] == 8000
