@@ -788,8 +788,8 @@ PROFILES = [
     ("sum_partials", "prefill_down_proj_7b", "sum_partials_kernel", "rest", None),
     ("slice_sumsq", "long_prefill_tp8_share", "slice_sumsq_kernel", "rest", None),
     ("slice_apply", "long_prefill_tp8_share", "slice_apply_kernel", "rest", None),
-    ("token_rows_gather", "long_prefill_tp8_share", "token_rows_kernel", "rest", "max"),
-    ("token_rows_shard", "long_prefill_tp8_share", "token_rows_kernel", "rest", "min"),
+    ("token_rows_gather", "long_prefill_tp8_share", "token_rows_kernel<true>", "rest", "max"),
+    ("token_rows_shard", "long_prefill_tp8_share", "token_rows_kernel<false>", "rest", "min"),
 ]
 PROFILE_NOTES = {
     "decode_fused_chunk": "single-launch decode path on rank 0's 4-row token chunk, both shards' products",

@@ -12,7 +12,7 @@
 //
 // Two kernels:
 //  * prefill: the four-wave form of the MFMA tile engine of gemm_nt.h
-//    (256 x 224 or 256 x 256 tiles, operands DMA'd straight to LDS, double-buffered) with
+//    (256 x 224 or 256 x 256 tiles, operands DMA'd straight to LDS in rings of K steps) with
 //    v_mfma_f32_16x16x32_bf16 and fp32 accumulators in accumulation registers; the
 //    output goes out with streaming stores, so it does not sit dirty in the memory-side
 //    cache when the chunk reduce streams its inputs;

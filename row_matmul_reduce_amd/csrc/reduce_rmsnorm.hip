@@ -33,7 +33,8 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// NT: streaming stores for both outputs (chunks of many rows; see st16_nt).
+// NT: streaming loads of the partials and the residual and streaming stores for both outputs
+// (chunks of many rows; see ld16_nt and st16_nt).
 template <int CPL, int RW, int ROWS, bool NT>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64 * RW * ROWS, 64 * RW * ROWS)))
 reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t *__restrict__ residual,
@@ -57,7 +58,8 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             const int c = t + j * 64 * RW;
-            rv[j] = c < nch ? ld16(residual + rbase + c * 8) : u32x4{0, 0, 0, 0};
+            rv[j] = c < nch ? (NT ? ld16_nt(residual + rbase + c * 8) : ld16(residual + rbase + c * 8))
+                            : u32x4{0, 0, 0, 0};
             gv[j] = c < nch ? ld16(gamma + c * 8) : u32x4{0, 0, 0, 0};
         }
         for (int s0 = 0; s0 < tp; s0 += G) {
@@ -67,7 +69,8 @@ reduce_rmsnorm_kernel(PartialPtrs P, int tp, int m_chunk, int n, const uint16_t 
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const int c = t + j * 64 * RW;
-                    v[q][j] = (s0 + q < tp && c < nch) ? ld16(P.p[s0 + q] + rbase + c * 8) : u32x4{0, 0, 0, 0};
+                    const uint16_t *src = P.p[s0 + q] + rbase + c * 8;
+                    v[q][j] = (s0 + q < tp && c < nch) ? (NT ? ld16_nt(src) : ld16(src)) : u32x4{0, 0, 0, 0};
                 }
 #pragma unroll
             for (int q = 0; q < G; ++q)

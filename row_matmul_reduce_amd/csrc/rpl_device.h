@@ -41,6 +41,12 @@ __device__ __forceinline__ void st8(void *p, u32x2 v) { *reinterpret_cast<u32x2 
 // 43 us after one that wrote the same bytes with these stores.
 __device__ __forceinline__ void st16_nt(void *p, u32x4 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p)); }
 __device__ __forceinline__ void st8_nt(void *p, u32x2 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x2 *>(p)); }
+// Streaming (non-temporal) load, for inputs read once in volumes beyond what the memory-side
+// cache could keep for a later reader.  Measured on MI355X (bench steps, inputs rotated beyond
+// twice that cache): the 230 MB long-prefill chunk reduce 43.8 -> 41.0 us, the 73 MB prefill chunk
+// reduce 14.7 -> 14.2 us, the 335 MB token-row gather 57.3 -> 54.2 us; not used where it measured
+// slower (the quantiser +3%, the all-reduce sum and the hidden-split step 1 +1-2%).
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)); }
 
 // Lane i of the result takes lane i + SH of v within each row of 16 lanes (zero past the
 // row): a DPP row shift, which moves an MFMA operand fragment between token-row lanes.

@@ -14,7 +14,9 @@
 // reduce is given every rank's partial.
 //
 // One workgroup per output row (rows grid-strided); a thread moves up to 4
-// 16-byte chunks of the row per pass, all loads issued before the stores.
+// 16-byte chunks of the row per pass, all loads issued before the stores.  The
+// gather, which moves every token row, loads with streaming loads (see ld16_nt);
+// the shard, one rank's block, with ordinary ones.
 #include "rpl_device.h"
 #include "rpl_launch.h"
 
@@ -22,6 +24,7 @@ namespace rpl {
 
 constexpr int TR_U = 4;
 
+template <bool NTL>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256)))
 token_rows_kernel(PartialPtrs src, int64_t ld, int rows_out, int n, int gather, int64_t row0, int m_src,
                   int m_chunk, uint16_t *__restrict__ out) {
@@ -40,7 +43,7 @@ token_rows_kernel(PartialPtrs src, int64_t ld, int rows_out, int n, int gather, 
 #pragma unroll
             for (int u = 0; u < TR_U; ++u) {
                 const int c = c0 + u * 256;
-                v[u] = (sp && c < nch) ? ld16(sp + c * 8) : u32x4{0, 0, 0, 0};
+                v[u] = (sp && c < nch) ? (NTL ? ld16_nt(sp + c * 8) : ld16(sp + c * 8)) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < TR_U; ++u) {
@@ -54,8 +57,12 @@ token_rows_kernel(PartialPtrs src, int64_t ld, int rows_out, int n, int gather, 
 static hipError_t launch_rows(const PartialPtrs &p, int64_t ld, int rows_out, int n, int gather, int64_t row0,
                               int m_src, int m_chunk, uint16_t *out, hipStream_t st) {
     const int grid = rows_out < 16384 ? rows_out : 16384;
-    hipLaunchKernelGGL(token_rows_kernel, dim3(grid), dim3(256), 0, st, p, ld, rows_out, n, gather, row0, m_src,
-                       m_chunk, out);
+    if (gather)
+        hipLaunchKernelGGL(token_rows_kernel<true>, dim3(grid), dim3(256), 0, st, p, ld, rows_out, n, gather, row0,
+                           m_src, m_chunk, out);
+    else
+        hipLaunchKernelGGL(token_rows_kernel<false>, dim3(grid), dim3(256), 0, st, p, ld, rows_out, n, gather, row0,
+                           m_src, m_chunk, out);
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ def test_rocprof_phase_selection():
              "reduce_rmsnorm_kernel<2, 8, 1, false>(x)", "read_ceiling_kernel(x)", "read_ceiling_kernel(x)",
              "gemm_bf16_wide_kernel<256, 3, false>(x)", "reduce_rmsnorm_kernel<3, 4, 1, true>(x)",
              "decode_fused_kernel<1, 4>(x)", "gemm_bf16_decode_kernel<4>(x)", "decode_fused_kernel<1, 2>(x)",
-             "sum_partials_kernel(x)", "token_rows_kernel(x)", "token_rows_kernel(x)"]
+             "sum_partials_kernel(x)", "token_rows_kernel<true>(x)", "token_rows_kernel<false>(x)"]
     grids = [65536, 2048, 65536, 1024, 57344, 57344, 57344, 1024, 65536, 131072, 65536, 512, 115712, 57344,
              115712, 4096, 8192, 4096]
     recs = [{"Kernel_Name": "void rpl::" + n, "Grid_Size": str(g), "Start_Timestamp": str(i)}
@@ -80,6 +80,7 @@ def test_rocprof_phase_selection():
     assert "<1, 4>" in sel[("decode_fused_chunk", "decode_o_proj_7b")][115712][0]["Kernel_Name"]
     assert list(sel[("token_rows_gather", "long_prefill_tp8_share")]) == [8192]
     assert list(sel[("token_rows_shard", "long_prefill_tp8_share")]) == [4096]
+    assert "<false>" in sel[("token_rows_shard", "long_prefill_tp8_share")][4096][0]["Kernel_Name"]
 
 
 def test_memory_path_summary(tmp_path):
