@@ -621,25 +621,38 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
         else:
             torch.matmul(d["x"], d["w"].t())
 
-    def timed(fn):
+    def timed(fn, sets):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(block)]
         for i, (a, b) in enumerate(evs):
-            d = path.sets[i % len(path.sets)]
+            d = sets[i % len(sets)]
             a.record()
             fn(d)
             b.record()
         torch.cuda.synchronize()
         return [a.elapsed_time(b) * 1e3 for a, b in evs]
 
-    for fn in (vendor, path.partial):
-        for i in range(5):
-            fn(path.sets[i % len(path.sets)])
-    torch.cuda.synchronize()
-    ours, theirs = [], []
-    for _ in range(rounds):
-        ours += timed(path.partial)
-        theirs += timed(vendor)
-    us, own = float(np.median(theirs)), float(np.median(ours))
+    def compare(sets, n_rounds):
+        for fn in (vendor, path.partial):
+            for i in range(5):
+                fn(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        ours, theirs = [], []
+        for _ in range(n_rounds):
+            ours += timed(path.partial, sets)
+            theirs += timed(vendor, sets)
+        return float(np.median(theirs)), float(np.median(ours))
+
+    def load_of(sets):
+        # the card's clock and power while each GEMM runs back to back (outside the timed blocks)
+        load = {}
+        for name, fn in (("partial", path.partial), ("vendor", vendor)):
+            c = clocks_under_load(torch, lambda i, fn=fn: fn(sets[i % len(sets)]))
+            if c is not None:
+                load[name] = {"sclk_mhz": (c["sclk_mhz"] or {}).get("median"),
+                              "power_w": (c["power_w"] or {}).get("median"), "power_cap_w": c["power_cap_w"]}
+        return load or None
+
+    us, own = compare(path.sets, rounds)
     rate = wl.gemm_flops() / (us * 1e-6) / 1e12
     if path.w8:
         return {"what": "torch._int_mm (hipBLASLt) of the same int8 operands, [m,k] x [n,k]^T -> int32 (no "
@@ -647,18 +660,25 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
                         "per launch in alternating blocks, medians",
                 "us": us, "TOP/s": rate, "frac_int8_peak": rate / PEAK_I8_TOPS,
                 "partial_us_same_method": own, "partial_over_vendor_time": own / us}
-    # the card's clock and power while each GEMM runs back to back (outside the timed blocks)
-    load = {}
-    for name, fn in (("partial", path.partial), ("vendor", vendor)):
-        c = clocks_under_load(torch, lambda i, fn=fn: fn(path.sets[i % len(path.sets)]))
-        if c is not None:
-            load[name] = {"sclk_mhz": (c["sclk_mhz"] or {}).get("median"),
-                          "power_w": (c["power_w"] or {}).get("median"), "power_cap_w": c["power_cap_w"]}
+    load = load_of(path.sets)
+    # The same two GEMMs on all-zero operands of the same shapes (as many HBM-resident copies): the
+    # operands' bits hardly toggle, so the board's power cap does not bind and the clock stays near its
+    # maximum -- how fast each kernel's schedule is, apart from the power the data costs.
+    zsets = [{"x": torch.zeros_like(path.sets[0]["x"]), "w": torch.zeros_like(path.sets[0]["w"])}
+             for _ in range(len(path.sets))]
+    zus, zown = compare(zsets, max(2, rounds // 2))
+    zero = {"what": "both GEMMs on all-zero operands of the same shapes and rotation (context: the clock "
+                    "without the power the data's bit activity costs)",
+            "vendor_us": zus, "partial_us": zown,
+            "partial_TFLOP/s": wl.gemm_flops() / (zown * 1e-6) / 1e12,
+            "partial_frac_bf16_peak": wl.gemm_flops() / (zown * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+            "partial_over_vendor_time": zown / zus, "clock_and_power_under_load": load_of(zsets)}
+    del zsets
     return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation; it and "
                     "the library's partial timed per launch in alternating blocks, medians",
             "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS,
             "partial_us_same_method": own, "partial_over_vendor_time": own / us,
-            "clock_and_power_under_load": load or None}
+            "clock_and_power_under_load": load, "zero_operands": zero}
 
 
 def cpu_baseline(wl, budget_s: float, dynamic: bool = False):
