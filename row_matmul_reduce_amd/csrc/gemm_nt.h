@@ -369,6 +369,12 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
         const float *srow = stage_area + p * STAGE_FLOATS, *scol = srow + BM;  // staged Ops only
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last steps' out-of-range DMAs into LDS
         __syncthreads();  // every wave's DMAs have landed and its fragment reads are done
+        // The lane's first byte in the copy, formed here from a lane index the compiler cannot see
+        // through: hoisted to the kernel's start, the per-row addresses outlive the K loop in
+        // scratch memory, and each reload here is a memory round trip.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const uint32_t cbase = (uint32_t)((wm0 + (ln & 15)) * ROWB + (wn0 + (ln >> 4) * 4) * 2);
 #pragma unroll
         for (int a = 0; a < FM; ++a)
 #pragma unroll
@@ -379,7 +385,7 @@ __device__ __forceinline__ void gemm_nt_wide(const GemmShape &g, const Op &op, u
                     v = op.pack_staged(acc[a][b], srow[r], *reinterpret_cast<const f32x4 *>(scol + c));
                 else
                     v = Op::pack(acc[a][b]);
-                *reinterpret_cast<u32x2 *>(smem + r * ROWB + c * 2) = v;
+                *reinterpret_cast<u32x2 *>(smem + cbase + (a * 16 * ROWB + b * 16 * 2)) = v;
             }
         __syncthreads();
         // Each thread stores PER chunks, in batches of SB whose LDS reads are all issued before
