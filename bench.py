@@ -606,7 +606,7 @@ def token_rows(torch, rpl, copies: int):
                            "shard_frac_hbm": bs / (us_s * 1e-6) / 1e9 / PEAK_HBM_GBS}}
 
 
-def library_reference(path, torch, rounds: int = 6, block: int = 20):
+def library_reference(path, torch, rounds: int = 6, block: int = 20, zero: bool = True):
     """Context only, not part of the path: the vendor GEMM on the same HBM-resident input sets --
     torch.matmul (hipBLASLt, bf16) for the bf16 partial, torch._int_mm (hipBLASLt, int8 x int8 ->
     int32, without the scales and with twice the output bytes) for the w8a8 partial.  It and the
@@ -661,6 +661,12 @@ def library_reference(path, torch, rounds: int = 6, block: int = 20):
                 "us": us, "TOP/s": rate, "frac_int8_peak": rate / PEAK_I8_TOPS,
                 "partial_us_same_method": own, "partial_over_vendor_time": own / us}
     load = load_of(path.sets)
+    if not zero:
+        return {"what": "torch.matmul (hipBLASLt) of the same operands, [m,k] x [n,k]^T, same input rotation; it "
+                        "and the library's partial timed per launch in alternating blocks, medians",
+                "us": us, "TFLOP/s": rate, "frac_bf16_peak": rate / PEAK_BF16_TFLOPS,
+                "partial_us_same_method": own, "partial_over_vendor_time": own / us,
+                "clock_and_power_under_load": load, "zero_operands": None}
     # The same two GEMMs on all-zero operands of the same shapes (as many HBM-resident copies): the
     # operands' bits hardly toggle, so the board's power cap does not bind and the clock stays near its
     # maximum -- how fast each kernel's schedule is, apart from the power the data costs.
@@ -760,29 +766,29 @@ def _cpu_model() -> str:
 # <dir> is where rocprofv3 writes), then `python bench.py --rocprof-summary <dir>`.
 PROFILE_RUNS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats -f csv -d <dir>/trace -o bench -- "
-             "python3 /root/repo/bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+             "python3 /root/repo/bench.py --steps 10 --warmup 2 --no-cpu-baseline --no-zero-operands",
     "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/fetch -o run -- "
-             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
     "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/write -o run -- "
-             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
     "cal_fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE -f csv -d <dir>/cal_fetch -o run -- "
                  "python3 /root/repo/bench.py --copy-calibration",
     "cal_write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE -f csv -d <dir>/cal_write -o run -- "
                  "python3 /root/repo/bench.py --copy-calibration",
     "mfma": "cd /tmp && rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT -f csv "
-            "-d <dir>/mfma -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+            "-d <dir>/mfma -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
     # memory-path and wait counters of the bf16 partials and hipBLASLt, three passes (each within the
     # per-block counter limits of one pass)
     "mem_a": "cd /tmp && rocprofv3 --pmc SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VMEM "
              "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS -f csv -d <dir>/mem_a -o run -- "
-             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
     "mem_b": "cd /tmp && rocprofv3 --pmc TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum TD_TD_BUSY_sum TD_TC_STALL_sum "
              "TCP_PENDING_STALL_CYCLES_sum TCP_TCC_READ_REQ_sum TCP_TOTAL_CACHE_ACCESSES_sum GRBM_GUI_ACTIVE -f csv "
-             "-d <dir>/mem_b -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "-d <dir>/mem_b -o run -- python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
     "mem_c": "cd /tmp && rocprofv3 --pmc SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE "
              "SQ_ACTIVE_INST_LDS SQ_INST_LEVEL_VMEM SQ_INST_CYCLES_VMEM_RD SQ_INSTS_MFMA TA_DATA_STALLED_BY_TC_CYCLES_sum "
              "TA_ADDR_STALLED_BY_TD_CYCLES_sum TD_TCP_STALL_CYCLES_sum TD_SPI_STALL_sum -f csv -d <dir>/mem_c -o run -- "
-             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline",
+             "python3 /root/repo/bench.py --steps 4 --warmup 1 --no-cpu-baseline --no-zero-operands",
 }
 # The default run's phases, in order, each opened by the first dispatch whose name matches (after the
 # previous phase opened): the main bf16 prefill step, the two w8a8 steps, the decode step, the
@@ -1139,6 +1145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill", choices=list(WORKLOAD_IDS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-zero-operands", action="store_true",
+                    help="skip the vendor comparison's runs on all-zero operands (the profile passes use this, so "
+                         "that every dispatch they summarise ran on the workload's data)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-side", action="store_true",
                     help="skip the side paths (w8a8, w8a8_dynamic, decode, long prefill)")
@@ -1204,7 +1213,7 @@ def main():
     sets_used = len(path.sets)
     reference = None
     if not path.w8 and not small and not args.no_side:
-        reference = library_reference(path, torch)
+        reference = library_reference(path, torch, zero=not args.no_zero_operands)
     del path
     torch.cuda.empty_cache()
 
@@ -1225,7 +1234,7 @@ def main():
                 kp["plain_read_ceiling"] = ceil
                 kp["frac_of_ceiling"] = ceil["us"] / kp["us"]
             if key in ("long_prefill", "w8a8"):
-                side[key]["library_reference"] = library_reference(sp, torch)
+                side[key]["library_reference"] = library_reference(sp, torch, zero=not args.no_zero_operands)
             del sp
             torch.cuda.empty_cache()
 
