@@ -1148,7 +1148,7 @@ def main():
     ap.add_argument("--no-zero-operands", action="store_true",
                     help="skip the vendor comparison's runs on all-zero operands (the profile passes use this, so "
                          "that every dispatch they summarise ran on the workload's data)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=25.0, help="seconds of oracle work for cpu_baseline (the pilot estimate runs long: about half of it is spent)")
     ap.add_argument("--no-side", action="store_true",
                     help="skip the side paths (w8a8, w8a8_dynamic, decode, long prefill)")
     ap.add_argument("--copies", type=int, default=0,
