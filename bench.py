@@ -27,7 +27,10 @@ warmup steps, untimed steps run for half a second so that the card is at its wor
 The JSON line reports the main step's algorithmic TFLOP/s, per-kernel times
 from HIP events on the launch stream, the roofline of the dominant kernel, the
 SCLK / MCLK levels sampled from sysfs while the same steps run, and the CPU
-oracle timed on a bounded sample of the same work.
+oracle timed on a bounded sample of the same work.  For the GEMM paths it also
+times the partials' MFMA instruction alone on random operands (mfma_ceiling): under
+the board's power cap that, not the published peak, is what the card sustains with
+real data, and each partial's fraction of it is reported beside its roofline.
 """
 from __future__ import annotations
 
@@ -399,6 +402,47 @@ def plain_read_ceiling(torch, rpl, tensors, launches: int = 200):
             "GB/s": nbytes / (grids[best] * 1e-6) / 1e9,
             "frac_hbm": nbytes / (grids[best] * 1e-6) / 1e9 / PEAK_HBM_GBS,
             "us_by_grid": grids, "torch_row_sum_us": t_sum}
+
+
+def mfma_power_ceiling(torch, rpl, launches: int = 3, iters: int = 40000):
+    """The MFMA instruction of each partial alone (rpl_mfma_ceiling, measurement only: 256 workgroups of
+    four waves, the engine's 128 x 128 wave tile in accumulation registers, no memory traffic) on random
+    operands, i.e. the rate the board's power cap allows with real data in the operands, and for bf16 also
+    on zeros (the clock without the data's power).  Event-timed medians of `launches` launches of about
+    40 ms; the chip's clock and each XCD's from the shader-clock and 100 MHz tick counts of every
+    workgroup (workgroup b runs on XCD b mod 8)."""
+    nb = rpl.MFMA_CEILING_OPS_BYTES
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260607)
+    ops = {"bf16_random": (0, torch.randn(nb // 2, device="cuda", generator=g).to(torch.bfloat16)),
+           "bf16_zero": (0, torch.zeros(nb, dtype=torch.uint8, device="cuda")),
+           "i8_random": (1, torch.randint(-127, 128, (nb,), device="cuda", dtype=torch.int8, generator=g))}
+    clocks = torch.zeros(512, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {"what": "rpl_mfma_ceiling: v_mfma_f32_16x16x32_bf16 / v_mfma_i32_16x16x64_i8 alone on 256 workgroups "
+                   "of four waves, two alternating operand sets per lane (random normal bf16, uniform int8 in "
+                   "[-127, 127], or zeros), no memory traffic; medians of %d event-timed launches of %d x 128 "
+                   "MFMAs per wave" % (launches, iters)}
+    for name, (kind, t) in ops.items():
+        rpl.rpl_mfma_ceiling(t, kind, max(1, iters // 10), clocks, sink)
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(launches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rpl.rpl_mfma_ceiling(t, kind, iters, clocks, sink)
+            b.record()
+            torch.cuda.synchronize()
+            c = clocks.view(256, 2).cpu().double()
+            xcd = [float(c[x::8, 0].sum() / c[x::8, 1].sum()) * 0.1 for x in range(8)]
+            runs.append((a.elapsed_time(b) * 1e3, float(c[:, 0].sum() / c[:, 1].sum()) * 0.1, xcd))
+        runs.sort(key=lambda r: r[0])
+        us, ghz, xcd = runs[len(runs) // 2]
+        unit = "TOP/s" if kind else "TFLOP/s"
+        rate = 256 * 4 * 128 * iters * (32768 if kind else 16384) / (us * 1e-6) / 1e12
+        out[name] = {"us": us, unit: rate, "frac_peak": rate / (PEAK_I8_TOPS if kind else PEAK_BF16_TFLOPS),
+                     "clock_ghz": ghz, "xcd_clock_ghz": xcd, "xcd_clock_spread": max(xcd) / min(xcd) - 1}
+    return out
 
 
 def _graph_mean_us(torch, fn, n_sets: int, launches: int = 100):
@@ -1211,6 +1255,7 @@ def main():
                     "unit": "TOP/s" if path.w8 else "TFLOP/s", "frac": rate / peak,
                     "traffic": load_traffic(pn, wl.name)}
     sets_used = len(path.sets)
+    w8 = path.w8
     reference = None
     if not path.w8 and not small and not args.no_side:
         reference = library_reference(path, torch, zero=not args.no_zero_operands)
@@ -1247,6 +1292,19 @@ def main():
         side.update(token_rows(torch, rpl, args.copies))
         torch.cuda.empty_cache()
 
+    ceiling = None
+    if not small:  # the GEMM partials against what their MFMA instruction alone sustains here
+        ceiling = mfma_power_ceiling(torch, rpl)
+        torch.cuda.empty_cache()
+        kernels[pn]["frac_of_power_limited_mfma_ceiling"] = roofline["achieved"] / ceiling[
+            "i8_random" if w8 else "bf16_random"][roofline["unit"]]
+        for key, ck, u in (("w8a8", "i8_random", "TOP/s"), ("w8a8_dynamic", "i8_random", "TOP/s"),
+                           ("long_prefill", "bf16_random", "TFLOP/s")):
+            kp = side.get(key, {}).get("kernels", {})
+            for kname in ("partial_w8a8", "partial_bf16"):
+                if kname in kp and u in kp[kname]:
+                    kp[kname]["frac_of_power_limited_mfma_ceiling"] = kp[kname][u] / ceiling[ck][u]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_budget, dynamic=args.workload == "w8a8_dynamic")
@@ -1260,7 +1318,7 @@ def main():
                    "n": wl.n, "m_chunk": wl.m_chunk, "parallelism": f"one TP rank of {wl.tp} (peers emulated)",
                    "input_sets_rotated": sets_used},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "clocks": clocks, "side": side,
-        "library_reference": reference,
+        "library_reference": reference, "mfma_ceiling": ceiling,
         "kernel_sources_sha256_16": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)

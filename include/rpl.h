@@ -414,7 +414,7 @@ rpl_status rpl_gather_rows(const rpl_bf16 *const *chunks, int32_t tp, int64_t m_
 /* Static, NUL-terminated name of a status code ("RPL_OK", ...; "unknown"). */
 const char *rpl_status_string(rpl_status s);
 
-/* Library ABI version: (major << 16) | minor.  Currently 2.1. */
+/* Library ABI version: (major << 16) | minor.  Currently 2.2. */
 int32_t rpl_version(void);
 
 #ifdef __cplusplus

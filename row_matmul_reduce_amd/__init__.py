@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.rpl_gather_rows.argtypes = [_p, _i32, _i64, _i64, _i64, _i64, _p, _p]
         L.rpl_read_ceiling.restype = ctypes.c_int
         L.rpl_read_ceiling.argtypes = [_p, _i64, _i32, _p, _p]
+        L.rpl_mfma_ceiling.restype = ctypes.c_int
+        L.rpl_mfma_ceiling.argtypes = [_p, _i64, _i32, _i32, _p, _p, _p]
         L.rpl_status_string.restype = ctypes.c_char_p
         L.rpl_status_string.argtypes = [ctypes.c_int]
         L.rpl_version.restype = ctypes.c_int32
@@ -431,6 +433,24 @@ def rpl_read_ceiling(t, grid: int, sink, stream=None):
     _check("rpl_read_ceiling", st)
 
 
+MFMA_CEILING_OPS_BYTES = 256 * 256 * 512
+
+
+def rpl_mfma_ceiling(ops, kind: int, iters: int, clocks, sink, stream=None):
+    """Measurement only: 256 workgroups of four waves issue iters x 128 MFMAs per wave on operands
+    taken from device tensor ops (at least MFMA_CEILING_OPS_BYTES bytes): kind 0 the bf16
+    v_mfma_f32_16x16x32_bf16, kind 1 the int8 v_mfma_i32_16x16x64_i8.  clocks (device int64, 512
+    entries) receives per workgroup the shader-clock and 100 MHz ticks of its MFMA loop; sink is a
+    device int32 tensor of at least one element."""
+    if not ops.is_cuda or not clocks.is_cuda or not sink.is_cuda or not ops.is_contiguous():
+        raise ValueError("device tensors, ops contiguous")
+    if clocks.numel() * clocks.element_size() < 512 * 8 or not clocks.is_contiguous():
+        raise ValueError("clocks must hold 512 contiguous 8-byte entries")
+    st = lib().rpl_mfma_ceiling(ops.data_ptr(), ops.numel() * ops.element_size(), int(kind), int(iters),
+                                clocks.data_ptr(), sink.data_ptr(), _stream(ops, stream))
+    _check("rpl_mfma_ceiling", st)
+
+
 def rpl_matmul_reduce_rmsnorm_noalloc(x_shards, w_shards, residual, gamma, eps: float, y, residual_out,
                                       stream=None):
     """rpl_matmul_reduce_rmsnorm without a workspace, for callers that cannot allocate: the
@@ -465,5 +485,5 @@ __all__ = ["rpl_partial", "rpl_reduce_chunk_rmsnorm", "rpl_w8a8_partial", "rpl_q
            "rpl_matmul_reduce_rmsnorm", "rpl_matmul_reduce_rmsnorm_workspace", "rpl_matmul_reduce_rmsnorm_status",
            "rpl_matmul_reduce_rmsnorm_set_poll_bound", "rpl_matmul_reduce_rmsnorm_noalloc", "rpl_sum_partials",
            "rpl_reduce_slice_sumsq", "rpl_rmsnorm_slice_apply",
-           "rpl_status_string", "rpl_version", "rpl_read_ceiling",
+           "rpl_status_string", "rpl_version", "rpl_read_ceiling", "rpl_mfma_ceiling", "MFMA_CEILING_OPS_BYTES",
            "RplError", "lib", "m_pad_of", "LIB_PATH"]

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "librpl.so")
 ARCH = "gfx950"
 
 SOURCES = ["rpl_api.cpp", "gemm_bf16.hip", "gemm_w8a8.hip", "reduce_rmsnorm.hip", "quant_per_token.hip", "decode_fused.hip",
-           "reduce_variants.hip", "token_rows.hip", "read_ceiling.hip"]
+           "reduce_variants.hip", "token_rows.hip", "read_ceiling.hip", "mfma_ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -400,6 +400,6 @@ const char *rpl_status_string(rpl_status s) {
     return "unknown";
 }
 
-int32_t rpl_version(void) { return (2 << 16) | 1; }
+int32_t rpl_version(void) { return (2 << 16) | 2; }
 
 }  // extern "C"

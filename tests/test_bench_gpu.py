@@ -35,3 +35,11 @@ def test_bench_json_line():
     # the whole step (partial + reduce) cannot run faster than its partial alone
     part = d["kernels"]["partial_bf16"]
     assert d["value"] <= part["TFLOP/s"] * 1.05
+    # the MFMA instruction alone: below the dense peak, and the partial below it
+    mc = d["mfma_ceiling"]
+    for name, unit in (("bf16_random", "TFLOP/s"), ("bf16_zero", "TFLOP/s"), ("i8_random", "TOP/s")):
+        e = mc[name]
+        assert 0 < e["frac_peak"] <= 1.0 and e[unit] > 0, (name, e)
+        assert 0.5 < e["clock_ghz"] < 3.0 and len(e["xcd_clock_ghz"]) == 8, (name, e)
+        assert all(0.5 < c < 3.0 for c in e["xcd_clock_ghz"]) and e["xcd_clock_spread"] >= 0
+    assert 0 < part["frac_of_power_limited_mfma_ceiling"] < 1.05

@@ -56,7 +56,7 @@ def test_status_strings_and_version():
     assert [rpl.rpl_status_string(s) for s in range(5)] == [
         "RPL_OK", "RPL_ERR_NULL", "RPL_ERR_INVALID", "RPL_ERR_UNSUPPORTED", "RPL_ERR_LAUNCH"]
     assert rpl.rpl_status_string(99) == "unknown"
-    assert rpl.rpl_version() == (2 << 16) | 1
+    assert rpl.rpl_version() == (2 << 16) | 2
 
 
 class Buf:
@@ -428,6 +428,26 @@ def test_read_ceiling_validation():
     assert call(B.ptr + 8, 4080, 256, S.ptr) == UNSUP
     assert call(B.ptr, 4096, 256, S.ptr + 2) == UNSUP
     assert B.untouched() and S.untouched()
+
+
+def test_mfma_ceiling_validation():
+    """The MFMA measurement helper checks its arguments on the host before any HIP call."""
+    L = rpl.lib()
+    B, C, S = Buf(4096), Buf(4096), Buf(64)
+    need = rpl.MFMA_CEILING_OPS_BYTES
+    call = lambda p, nbytes, kind, iters, c, s: L.rpl_mfma_ceiling(p, nbytes, kind, iters, c, s, None)
+    assert call(None, need, 0, 10, C.ptr, S.ptr) == NULL
+    assert call(B.ptr, need, 0, 10, None, S.ptr) == NULL
+    assert call(B.ptr, need, 0, 10, C.ptr, None) == NULL
+    assert call(B.ptr, need - 16, 0, 10, C.ptr, S.ptr) == INVALID
+    assert call(B.ptr, need, 2, 10, C.ptr, S.ptr) == INVALID
+    assert call(B.ptr, need, -1, 10, C.ptr, S.ptr) == INVALID
+    assert call(B.ptr, need, 0, 0, C.ptr, S.ptr) == INVALID
+    assert call(B.ptr, need, 1, (1 << 20) + 1, C.ptr, S.ptr) == INVALID
+    assert call(B.ptr + 8, need, 0, 10, C.ptr, S.ptr) == UNSUP
+    assert call(B.ptr, need, 0, 10, C.ptr + 4, S.ptr) == UNSUP
+    assert call(B.ptr, need, 1, 10, C.ptr, S.ptr + 2) == UNSUP
+    assert B.untouched() and C.untouched() and S.untouched()
 
 
 def test_fused_noalloc_validation():
