@@ -52,8 +52,11 @@ mfma_ceiling_kernel(const u32x4 *__restrict__ ops, int iters, uint64_t *__restri
                     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i / 8][i % 8]) : "v"(b[s][i % 8]), "v"(a[s][i / 8]));
             }
     }
-    // the last MFMAs' results are read below; the wait states cover their latency
+    // the last eight MFMAs' results are read below: the wait states come after all of them
+    // and before any read (the empty statements order the other seven behind the wait)
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[7][7]));
+#pragma unroll
+    for (int j = 0; j < 7; ++j) asm volatile("" : "+a"(acc[7][j]));
     const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
     uint32_t fold = 0;
 #pragma unroll
