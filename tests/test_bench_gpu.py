@@ -43,3 +43,26 @@ def test_bench_json_line():
         assert 0.5 < e["clock_ghz"] < 3.0 and len(e["xcd_clock_ghz"]) == 8, (name, e)
         assert all(0.5 < c < 3.0 for c in e["xcd_clock_ghz"]) and e["xcd_clock_spread"] >= 0
     assert 0 < part["frac_of_power_limited_mfma_ceiling"] < 1.05
+
+
+def test_mfma_ceiling_helper():
+    """The MFMA measurement helper on both instructions: every workgroup reports its loop's shader-clock
+    and 100 MHz ticks, and the clock they give lies in the card's range."""
+    import torch
+    import row_matmul_reduce_amd as rpl
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    nb = rpl.MFMA_CEILING_OPS_BYTES
+    ops = torch.randint(-127, 128, (nb,), dtype=torch.int8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for kind in (0, 1):
+        print(f"[mfma_ceiling] kind={kind} iters=200", flush=True)
+        clocks = torch.zeros(512, dtype=torch.int64, device="cuda")
+        rpl.rpl_mfma_ceiling(ops, kind, 200, clocks, sink)
+        torch.cuda.synchronize()
+        c = clocks.view(256, 2).cpu()
+        assert bool((c > 0).all()), "every workgroup wrote its ticks"
+        ghz = c[:, 0].double() / c[:, 1].double() * 0.1
+        assert bool(((ghz > 0.3) & (ghz < 3.0)).all()), ghz
+    with pytest.raises(rpl.RplError):
+        rpl.rpl_mfma_ceiling(ops[:nb - 16], 0, 10, clocks, sink)
