@@ -45,6 +45,9 @@ SMALL_SHAPES = [
     (7, 72, 2608, 2),      # decode kernel, m_pad = 8: two K steps per activation load, K tail
     (2, 24, 1040, 1),      # decode kernel, m_pad = 2, 32.5 K steps
     (8, 3584, 3584, 2),    # decode o_proj shape
+    (8, 3576, 3584, 2),    # decode kernel, the last 16-column block 8 wide
+    (6, 5120, 2048, 2),    # decode kernel, 320 workgroups (more than the CUs)
+    (3, 4104, 512, 1),     # decode kernel, the last 16-column block 8 wide, m_pad = 3
     (17, 64, 128, 8),      # tile kernel with bounds checks, m_pad = 24, a single K step
     (300, 520, 656, 2),    # ragged m, n and K (k_shard = 328)
     (257, 264, 288, 4),    # m_pad = 260: one row past a 256-row tile
